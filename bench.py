@@ -1,0 +1,246 @@
+"""Benchmark of the KSA hot path on one MI355X.
+
+One step = one pass of the whole path on synthetic inputs already resident
+in HBM:
+  1. RoPE pre-pass (KSA position rule) over Q and K of the 32K-token prefill,
+  2. KSA prefill attention (32K text tokens, k=8, w=64, 32/8 heads, d=128, bf16),
+  3. hand-off of that prefill's K/V into its decode cache (bulk fill),
+  4. one decode step of the 64-sequence, 131072-token-history batch
+     (text-token cache append, then split-K decode over the contiguous slice).
+
+``value`` is the prefill throughput in TFLOP/s counted over visible
+(query, key) pairs only, 2 (Dqk + Dv) Hq per pair; the decode step's HBM
+throughput is reported beside it.  Kernel times come from HIP events on the
+stream every launch goes to.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "KSA prefill TFLOP/s (visible pairs) + decode HBM GB/s, 1 MI355X, % roofline"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+
+
+def visible_pairs(n: int, k: int, C: int) -> int:
+    """Visible (query, key) pairs of one head: every summary sees k+1 keys;
+    text token i in chunk c sees min(c, C) k + (i mod k) + 1 text keys and
+    max(0, c - C) summaries.  Summed in closed form over whole chunks."""
+    M = n // k
+    tot = M * (k + 1)
+
+    def text_rows(c0: int, c1: int, rows_per_chunk: int) -> int:
+        # sum over chunks c in [c0, c1) of sum_{p<rows} (min(c,C) k + p + 1 + max(0, c-C))
+        s = 0
+        for lo, hi in ((c0, min(c1, C)), (max(c0, C), c1)):
+            if hi <= lo:
+                continue
+            cnt = hi - lo
+            csum = (lo + hi - 1) * cnt // 2
+            if lo >= C:   # min(c,C) = C, max(0,c-C) = c - C
+                per = C * k * cnt + (csum - C * cnt)
+            else:         # min(c,C) = c, max = 0
+                per = k * csum
+            s += per * rows_per_chunk + cnt * rows_per_chunk * (rows_per_chunk + 1) // 2
+        return s
+
+    tot += text_rows(0, M, k)
+    rem = n - M * k
+    if rem:
+        tot += text_rows(M, M + 1, rem)
+    return tot
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0 = auto)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; multi-GPU runs are not part of it",
+                          "n_gpus": args.gpus}))
+        return 2
+
+    import torch
+
+    import kv_cache_compression_amd as ksa
+    import ksa_synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    # ---- prefill workload: 32K text tokens ----
+    w = ksa_synth.PREFILL_32K
+    L = ksa.ksa_augmented_len(w.n_text, w.chunk)
+    q, kx, v = ksa_synth.prefill_qkv(w, L)
+    p = ksa.Params(w.chunk, w.window, w.hq, w.hkv, w.dqk, w.dv, w.dtype)
+    qd, kd, vd = q.to(dev), kx.to(dev), v.to(dev)
+    del q, kx, v
+    out = torch.empty((1, L, w.hq, w.dv), dtype=w.dtype, device=dev)
+    pcache = ksa.Cache(p, 1, w.n_text // w.chunk, device=dev)
+    pairs = visible_pairs(w.n_text, w.chunk, w.window)
+    flops = 2 * (w.dqk + w.dv) * w.hq * pairs * w.batch
+    rope_bytes = 2 * 2 * L * (w.hq + w.hkv) * w.dqk            # read + write Q and K
+    fill_rows = 1 + w.chunk + w.window * w.chunk + w.n_text // w.chunk
+
+    # ---- decode workload: 64 sequences x 131072-token history ----
+    dw = ksa_synth.DECODE_GQA
+    dp = ksa.Params(dw.chunk, dw.window, dw.hq, dw.hkv, dw.dqk, dw.dv, dw.dtype)
+    hist = ksa_synth.decode_histories(dw)      # text tokens incl. the query
+    max_s = max(n // dw.chunk for n in hist) + 1
+    dcache = ksa.Cache(dp, dw.batch, max_s, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(dw.seed)
+    dcache.k.normal_(generator=gen)
+    dcache.v.normal_(generator=gen)
+    st0 = torch.zeros((dw.batch, 4), dtype=torch.int32)
+    for b, n in enumerate(hist):
+        m = (n - 1) // dw.chunk
+        st0[b, 0] = m
+        st0[b, 1] = n - 1 - m * dw.chunk            # fill before the query token arrives
+    st0 = st0.to(dev)
+    g2 = ksa_synth.gen(dw.seed + 7)
+    k_new = ksa_synth.normal((dw.batch, dw.hkv, dw.dqk), dw.dtype, g2).to(dev)
+    v_new = ksa_synth.normal((dw.batch, dw.hkv, dw.dv), dw.dtype, g2).to(dev)
+    dq = ksa_synth.decode_query(dw).to(dev)
+    kind = torch.zeros((dw.batch,), dtype=torch.int32, device=dev)
+    dout = torch.empty((dw.batch, dw.hq, dw.dv), dtype=dw.dtype, device=dev)
+    ws = ksa.decode_workspace(dcache)
+    dec_rows = 0
+    for n in hist:
+        m = (n - 1) // dw.chunk
+        r = n - m * dw.chunk
+        dec_rows += r + min(m, dw.window) * dw.chunk + max(0, m - dw.window)
+    dec_bytes = (dec_rows * dw.hkv * (dw.dqk + dw.dv) * 2
+                 + dw.batch * dw.hq * (dw.dqk + dw.dv) * 2)  # cache slice + q + out
+    torch.cuda.synchronize()
+
+    segs = ["rope", "prefill", "fill", "append", "decode"]
+
+    def step(ev):
+        ev[0].record(stream)
+        ksa.ksa_rope_augmented(p, qd, w.n_text, w.rope_theta, stream=stream)
+        ksa.ksa_rope_augmented(p, kd, w.n_text, w.rope_theta, stream=stream)
+        ev[1].record(stream)
+        ksa.ksa_prefill_attn(p, qd, kd, vd, w.n_text, out=out, stream=stream)
+        ev[2].record(stream)
+        ksa.ksa_cache_fill(pcache, kd, vd, w.n_text, stream=stream)
+        ev[3].record(stream)
+        dcache.state.copy_(st0)
+        ksa.ksa_cache_append(dcache, k_new, v_new, kind, stream=stream)
+        ev[4].record(stream)
+        ksa.ksa_decode_attn(dcache, dq, kind, out=dout, workspace=ws, stream=stream)
+        ev[5].record(stream)
+
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    for _ in range(args.warmup):
+        step(mk())
+    torch.cuda.synchronize()
+    evs = [mk() for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    seg_ms = {s: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps for i, s in enumerate(segs)}
+    errs = ksa.ksa_cache_read_errors(dcache)
+    if any(errs):
+        raise RuntimeError(f"decode cache error bits {errs}")
+
+    pre_tflops = flops / (seg_ms["prefill"] * 1e-3) / 1e12
+    dec_gbps = dec_bytes / (seg_ms["decode"] * 1e-3) / 1e9
+    rope_gbps = rope_bytes / (seg_ms["rope"] * 1e-3) / 1e9
+
+    res = {
+        "metric": METRIC,
+        "value": round(pre_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q/K/V and cache)",
+        "config": {
+            "workload": w.name + " + " + dw.name,
+            "prefill": {"batch": w.batch, "n_text": w.n_text, "augmented_len": L, "chunk": w.chunk,
+                        "window_chunks": w.window, "q_heads": w.hq, "kv_heads": w.hkv, "head_dim": w.dqk,
+                        "rope_theta": w.rope_theta, "visible_pairs_per_head": pairs, "flops": flops},
+            "decode": {"batch": dw.batch, "history_text_tokens": hist[0] - hist[0] % dw.chunk,
+                       "chunk": dw.chunk, "window_chunks": dw.window, "q_heads": dw.hq,
+                       "kv_heads": dw.hkv, "head_dim": dw.dqk, "slice_rows_total": dec_rows,
+                       "bytes": dec_bytes},
+        },
+        "decode": {"value": round(dec_gbps, 1), "unit": "GB/s", "frac_of_peak": round(dec_gbps / PEAK_HBM_GBPS, 4),
+                   "ms": round(seg_ms["decode"], 4)},
+        "rope": {"value": round(rope_gbps, 1), "unit": "GB/s", "ms": round(seg_ms["rope"], 4)},
+        "breakdown_ms": {s: round(v, 4) for s, v in seg_ms.items()},
+        "roofline": {"kernel": "prefill_mfma_d128_kernel", "bound": "mfma", "achieved": round(pre_tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def cpu_baseline(w, rows_req: int) -> dict:
+    """The fp64 oracle on a bounded sample of the same prefill workload."""
+    import numpy as np
+    import torch
+
+    import ksa_synth
+    from oracle import ksa_oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    L = O.augmented_len(w.n_text, w.chunk)
+    q, kx, v = ksa_synth.prefill_qkv(w, L)
+    pos = O.position_ids(w.n_text, w.chunk)
+    kr = O.rope_rotate(kx[0].double().numpy(), pos, w.rope_theta)
+    vv = v[0].double().numpy()
+    scale = 1.0 / math.sqrt(w.dqk)
+    mask_count = lambda rows: int(O.visibility_mask_fast(w.n_text, w.chunk, w.window, rows=rows).sum())
+
+    def run(nrows):
+        rows = np.linspace(0, L - 1, nrows).astype(np.int64)
+        qs = np.zeros((L, w.hq, w.dqk))
+        qs[rows] = O.rope_rotate(q[0, rows].double().numpy(), pos[rows], w.rope_theta)
+        t0 = time.perf_counter()
+        O.ksa_attention(qs, kr, vv, w.n_text, w.chunk, w.window, scale, rows=rows, row_block=64)
+        dt = time.perf_counter() - t0
+        return rows, dt
+
+    nrows = rows_req or 16
+    rows, dt = run(nrows)
+    if not rows_req:   # scale the sample to about 15 s of oracle work
+        nrows = int(min(4096, max(16, nrows * 15.0 / max(dt, 1e-3))))
+        rows, dt = run(nrows)
+    fl = 2 * (w.dqk + w.dv) * w.hq * mask_count(rows)
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{len(rows)} evenly spaced augmented rows x {w.hq} heads of {w.name} "
+                      f"(fp64, dense masked rows), {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

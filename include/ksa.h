@@ -1,0 +1,185 @@
+/*
+ * ksa.h - C ABI of the Kwai Summary Attention (KSA) hot path for AMD gfx950.
+ *
+ * Method source: "Kwai Summary Attention Technical Report" (arXiv:2604.24432).
+ * The report defines:
+ *   - the augmented sequence: after every k text tokens one summary token,
+ *     chunk j = [t_jk .. t_jk+k-1, s_j]                     (Sec. 2.2.1, Eq. 1)
+ *   - summary visibility: a summary reads only its own chunk; its position
+ *     id equals the chunk's last text token's id           (Sec. 2.2.1)
+ *   - text visibility: the text of chunks floor(i/k)-C .. floor(i/k) up to
+ *     t_i, plus the summaries s_0 .. s_{floor(i/k)-C-1}     (Sec. 2.2.2, Eq. 2-3)
+ *   - masked softmax attention over that rule               (Sec. 4.1.4, Eq. 10)
+ *   - a block-sparse prefill kernel that loads only visible
+ *     blocks and never builds the mask                      (Sec. 2.3)
+ *   - a decode cache of three adjacent regions (current chunk | sliding
+ *     chunk ring | summary buffer) read as one contiguous slice, with the
+ *     lifecycle of Fig. 4b-4e                               (Sec. 2.3.1, Fig. 4)
+ *
+ * Readings fixed by this library where the report is silent:
+ *   - a summary token also sees itself (k+1 keys);
+ *   - C ("window_chunks") counts complete past chunks; the query's own chunk
+ *     is always visible; chunks with negative index do not exist;
+ *   - n need not be a multiple of k: the trailing partial chunk has no summary;
+ *   - query head h reads key/value head h / (Hq / Hkv);
+ *   - RoPE is half-split, angle = pos * theta^(-2f/rot_dim).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers unless a comment says "host".
+ *     Tensors are dense, row-major, in the layout given beside each argument.
+ *   - The caller owns every buffer.  The library allocates nothing, frees
+ *     nothing and does not synchronise, except ksa_cache_read_errors (which
+ *     is documented as synchronous).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every launch is asynchronous on that stream.
+ *   - Every function returning int32_t returns a ksa_status.  Host-detectable
+ *     problems (NULL pointers, bad sizes, unsupported shapes) are reported
+ *     before anything is launched; ksa_last_error_message() then holds a
+ *     thread-local description.  A failed launch returns KSA_STATUS_HIP_ERROR.
+ *   - Outputs are fully overwritten; inputs are never modified except the
+ *     in-place rotary calls and the cache state/regions.
+ */
+#ifndef KSA_H_
+#define KSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define KSA_API __attribute__((visibility("default")))
+#else
+#define KSA_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KSA_STATUS_OK = 0,
+  KSA_STATUS_INVALID_ARGUMENT = 1,
+  KSA_STATUS_UNSUPPORTED = 2,
+  KSA_STATUS_CAPACITY = 3,
+  KSA_STATUS_WORKSPACE_TOO_SMALL = 4,
+  KSA_STATUS_HIP_ERROR = 5
+} ksa_status;
+
+typedef enum { KSA_DTYPE_BF16 = 0, KSA_DTYPE_FP32 = 1 } ksa_dtype;
+
+/* Shape and rule parameters shared by every call. */
+typedef struct {
+  int32_t chunk_size;    /* k >= 1 (Eq. 1) */
+  int32_t window_chunks; /* C >= 0 complete past chunks seen as text (Eq. 2) */
+  int32_t num_q_heads;   /* Hq, a multiple of num_kv_heads */
+  int32_t num_kv_heads;  /* Hkv >= 1 */
+  int32_t head_dim_qk;   /* Dqk: 1..1024 generic; 128 and 576 have tuned kernels */
+  int32_t head_dim_v;    /* Dv <= Dqk when v_is_k_prefix */
+  int32_t v_is_k_prefix; /* 1: absorbed latent form, V = K[..., :Dv]; v pointers ignored */
+  float softmax_scale;   /* > 0; Eq. 10 uses 1/sqrt(d) */
+  int32_t dtype;         /* ksa_dtype of q/k/v/out/cache */
+} ksa_params;
+
+/* Decode cache of one layer.  Physical slot order of every (sequence, kv
+ * head), left to right (Fig. 4a):
+ *   slot 0                       scratch slot for the pending summary (Fig. 4c)
+ *   slots 1 .. k                 current chunk, filled right to left (Fig. 4b)
+ *   slots k+1 .. k+C*k           sliding-chunk ring, chunk j in ring slot j mod C (Fig. 4d)
+ *   slots k+1+C*k ..             summary buffer, s_0, s_1, ... (Fig. 4e)
+ * state[b*4 + 0] = m, committed chunks; state[b*4 + 1] = r, tokens in the
+ * current chunk (0..k); state[b*4 + 2] reserved (0); state[b*4 + 3] = error
+ * bits (KSA_CACHE_ERR_*).  Keys are stored after RoPE. */
+typedef struct {
+  void* k;               /* [batch, Hkv, slots, Dqk] */
+  void* v;               /* [batch, Hkv, slots, Dv]; NULL when v_is_k_prefix */
+  int32_t* state;        /* [batch, 4] int32 */
+  int32_t max_summaries; /* capacity of the summary buffer */
+} ksa_cache;
+
+enum {
+  KSA_CACHE_ERR_CHUNK_FULL = 1,      /* text append with r == k */
+  KSA_CACHE_ERR_CHUNK_NOT_FULL = 2,  /* summary append with r != k */
+  KSA_CACHE_ERR_SUMMARY_FULL = 4,    /* summary append with m == max_summaries */
+  KSA_CACHE_ERR_BAD_SUMMARY_READ = 8 /* summary decode without a just-committed chunk */
+};
+
+KSA_API const char* ksa_status_string(int32_t status);
+KSA_API const char* ksa_last_error_message(void);
+
+/* L = n + floor(n/k) (Eq. 1).  Returns -1 for n < 0 or k < 1. */
+KSA_API int64_t ksa_augmented_len(int64_t n_text, int32_t chunk_size);
+
+/* Half-split RoPE in place over the augmented sequence, positions by the
+ * KSA rule: text t_i -> i, summary s_j -> j*k + k - 1 (Sec. 2.2.1).
+ * x: [batch, L, num_heads, head_dim] in p->dtype.  Dims [rot_off,
+ * rot_off+rot_dim) are rotated, rot_dim even.  Angles are formed in fp64. */
+KSA_API int32_t ksa_rope_augmented(const ksa_params* p, int32_t batch, int64_t n_text, void* x,
+                           int32_t num_heads, int32_t head_dim, int32_t rot_off, int32_t rot_dim,
+                           double theta, void* stream);
+
+/* Same rotation with explicit positions: x [rows, num_heads, head_dim],
+ * positions [rows] int64 (device).  Used for decode tokens. */
+KSA_API int32_t ksa_rope_positions(const ksa_params* p, int64_t rows, const int64_t* positions, void* x,
+                           int32_t num_heads, int32_t head_dim, int32_t rot_off, int32_t rot_dim,
+                           double theta, void* stream);
+
+/* KSA prefill attention (Eq. 10 with the Eq. 1-3 rule), block-sparse:
+ * visible key tiles are enumerated from the chunk indices; no mask exists.
+ * Rows are in Eq. 1 order: row j*(k+1)+o is t_{jk+o} for o < k and s_j for
+ * o == k; the trailing n%k rows are text with no summary.
+ *   q   [batch, L, Hq,  Dqk]
+ *   k   [batch, L, Hkv, Dqk]
+ *   v   [batch, L, Hkv, Dv ]   (ignored when v_is_k_prefix)
+ *   out [batch, L, Hq,  Dv ]
+ *   lse [batch, Hq, L] fp32 natural-log normaliser, or NULL.
+ * bf16 with Dqk = Dv = 128 runs the MFMA kernel; other shapes the generic one. */
+KSA_API int32_t ksa_prefill_attn(const ksa_params* p, int32_t batch, int64_t n_text, const void* q,
+                         const void* k, const void* v, void* out, float* lse, void* stream);
+
+/* Slots per (sequence, kv head): 1 + k + C*k + max_summaries; -1 on bad input. */
+KSA_API int64_t ksa_cache_slots(const ksa_params* p, int32_t max_summaries);
+
+/* Empty every sequence: state := {0, 0, 0, 0}.  Regions are not cleared. */
+KSA_API int32_t ksa_cache_reset(const ksa_params* p, const ksa_cache* c, int32_t batch, void* stream);
+
+/* One decode-step cache update per sequence (Fig. 4b-4e).
+ *   k_new [batch, Hkv, Dqk], v_new [batch, Hkv, Dv] (post-RoPE keys)
+ *   kind  [batch] int32: 0 text token -> current-chunk slot k - r, r += 1;
+ *         1 summary -> scratch slot, copy the chunk into ring slot m mod C,
+ *           append at summary-buffer slot m, m += 1, r = 0;
+ *         -1 skip.
+ * Misuse (text into a full chunk, summary into a non-full chunk, summary
+ * buffer full) leaves that sequence untouched and sets its error bit. */
+KSA_API int32_t ksa_cache_append(const ksa_params* p, const ksa_cache* c, int32_t batch, const void* k_new,
+                         const void* v_new, const int32_t* kind, void* stream);
+
+/* Bulk hand-off from prefill: the result equals appending the L augmented
+ * rows one by one (text rows as kind 0, summary rows as kind 1), starting
+ * from an empty cache, for every sequence.
+ *   k_aug [batch, L, Hkv, Dqk], v_aug [batch, L, Hkv, Dv] (post-RoPE). */
+KSA_API int32_t ksa_cache_fill(const ksa_params* p, const ksa_cache* c, int32_t batch, int64_t n_text,
+                       const void* k_aug, const void* v_aug, void* stream);
+
+/* Bytes of workspace ksa_decode_attn needs for this batch and capacity. */
+KSA_API size_t ksa_decode_workspace_bytes(const ksa_params* p, int32_t batch, int32_t max_summaries);
+
+/* Split-K decode attention over one contiguous cache slice per sequence
+ * (Sec. 2.3.1): text query -> [current fill | ring | s_0 .. s_{m-C-1}],
+ * summary query -> [scratch | full current chunk].
+ *   q    [batch, Hq, Dqk] (post-RoPE)
+ *   kind [batch] int32: 0 text, 1 summary, -1 skip (outputs not written)
+ *   out  [batch, Hq, Dv];  lse [batch, Hq] fp32 or NULL
+ * An empty text slice yields out = 0, lse = -inf. */
+KSA_API int32_t ksa_decode_attn(const ksa_params* p, const ksa_cache* c, int32_t batch, const void* q,
+                        const int32_t* kind, void* out, float* lse, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* Synchronous: copies each sequence's error bits into host_error_bits[batch]
+ * (host memory) after the work queued on `stream` has finished. */
+KSA_API int32_t ksa_cache_read_errors(const ksa_params* p, const ksa_cache* c, int32_t batch,
+                              int32_t* host_error_bits, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KSA_H_ */

@@ -1,0 +1,284 @@
+// C ABI of the KSA library: argument checks, dispatch to the kernels.
+// Every entry point validates on the host before launching anything and
+// returns a ksa_status; details go to a thread-local message.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/ksa.h"
+#include "ksa_internal.h"
+
+namespace {
+
+thread_local char g_msg[512] = "";
+
+int32_t fail(ksa_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_msg, sizeof(g_msg), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+int32_t hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return KSA_STATUS_OK;
+  return fail(KSA_STATUS_HIP_ERROR, "%s: %s", where, hipGetErrorString(e));
+}
+
+int32_t check_params(const ksa_params* p) {
+  if (!p) return fail(KSA_STATUS_INVALID_ARGUMENT, "params is NULL");
+  if (p->chunk_size < 1) return fail(KSA_STATUS_INVALID_ARGUMENT, "chunk_size must be >= 1");
+  if (p->window_chunks < 0) return fail(KSA_STATUS_INVALID_ARGUMENT, "window_chunks must be >= 0");
+  if (p->num_q_heads < 1 || p->num_kv_heads < 1)
+    return fail(KSA_STATUS_INVALID_ARGUMENT, "head counts must be >= 1");
+  if (p->num_q_heads % p->num_kv_heads)
+    return fail(KSA_STATUS_INVALID_ARGUMENT, "num_q_heads (%d) must be a multiple of num_kv_heads (%d)",
+                p->num_q_heads, p->num_kv_heads);
+  if (p->head_dim_qk < 1 || p->head_dim_qk > 1024 || p->head_dim_v < 1 || p->head_dim_v > 1024)
+    return fail(KSA_STATUS_UNSUPPORTED, "head dims must be in [1, 1024]");
+  if (p->v_is_k_prefix && p->head_dim_v > p->head_dim_qk)
+    return fail(KSA_STATUS_INVALID_ARGUMENT, "head_dim_v exceeds head_dim_qk with v_is_k_prefix");
+  if (!(p->softmax_scale > 0.f)) return fail(KSA_STATUS_INVALID_ARGUMENT, "softmax_scale must be > 0");
+  if (p->dtype != KSA_DTYPE_BF16 && p->dtype != KSA_DTYPE_FP32)
+    return fail(KSA_STATUS_UNSUPPORTED, "dtype must be KSA_DTYPE_BF16 or KSA_DTYPE_FP32");
+  if (p->dtype == KSA_DTYPE_BF16 && ((p->head_dim_qk & 1) || (p->head_dim_v & 1)))
+    return fail(KSA_STATUS_UNSUPPORTED, "bf16 head dims must be even");
+  return KSA_STATUS_OK;
+}
+
+int32_t check_cache(const ksa_params* p, const ksa_cache* c) {
+  if (!c) return fail(KSA_STATUS_INVALID_ARGUMENT, "cache is NULL");
+  if (!c->k || !c->state) return fail(KSA_STATUS_INVALID_ARGUMENT, "cache k/state is NULL");
+  if (!p->v_is_k_prefix && !c->v) return fail(KSA_STATUS_INVALID_ARGUMENT, "cache v is NULL");
+  if (c->max_summaries < 0) return fail(KSA_STATUS_INVALID_ARGUMENT, "max_summaries < 0");
+  return KSA_STATUS_OK;
+}
+
+ksa::CacheArgs cache_args(const ksa_params* p, const ksa_cache* c, int32_t batch) {
+  ksa::CacheArgs a;
+  a.batch = batch;
+  a.k = p->chunk_size;
+  a.C = p->window_chunks;
+  a.hkv = p->num_kv_heads;
+  a.dqk = p->head_dim_qk;
+  a.dv = p->head_dim_v;
+  a.v_is_k_prefix = p->v_is_k_prefix;
+  a.max_summaries = c->max_summaries;
+  a.slots = 1 + static_cast<int64_t>(p->chunk_size) + static_cast<int64_t>(p->window_chunks) * p->chunk_size +
+            c->max_summaries;
+  return a;
+}
+
+ksa::DecodeArgs decode_args(const ksa_params* p, int32_t batch, int32_t max_summaries) {
+  ksa::DecodeArgs a;
+  a.batch = batch;
+  a.k = p->chunk_size;
+  a.C = p->window_chunks;
+  a.hq = p->num_q_heads;
+  a.hkv = p->num_kv_heads;
+  a.dqk = p->head_dim_qk;
+  a.dv = p->head_dim_v;
+  a.v_is_k_prefix = p->v_is_k_prefix;
+  a.max_summaries = max_summaries;
+  a.slots = 1 + static_cast<int64_t>(p->chunk_size) + static_cast<int64_t>(p->window_chunks) * p->chunk_size +
+            max_summaries;
+  a.scale = p->softmax_scale;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ksa_status_string(int32_t s) {
+  switch (s) {
+    case KSA_STATUS_OK: return "ok";
+    case KSA_STATUS_INVALID_ARGUMENT: return "invalid argument";
+    case KSA_STATUS_UNSUPPORTED: return "unsupported";
+    case KSA_STATUS_CAPACITY: return "capacity exceeded";
+    case KSA_STATUS_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case KSA_STATUS_HIP_ERROR: return "hip error";
+    default: return "unknown status";
+  }
+}
+
+const char* ksa_last_error_message(void) { return g_msg; }
+
+int64_t ksa_augmented_len(int64_t n_text, int32_t k) {
+  if (n_text < 0 || k < 1) return -1;
+  return n_text + n_text / k;
+}
+
+static int32_t rope_common(const ksa_params* p, ksa::RopeArgs& ra, void* x, void* stream) {
+  if (int32_t st = check_params(p)) return st;
+  if (!x) return fail(KSA_STATUS_INVALID_ARGUMENT, "x is NULL");
+  if (ra.heads < 1 || ra.head_dim < 1) return fail(KSA_STATUS_INVALID_ARGUMENT, "bad heads/head_dim");
+  if (ra.rot_dim < 2 || (ra.rot_dim & 1) || ra.rot_off < 0 || ra.rot_off + ra.rot_dim > ra.head_dim)
+    return fail(KSA_STATUS_INVALID_ARGUMENT, "rotary block [%d, %d) does not fit head_dim %d (even width)",
+                ra.rot_off, ra.rot_off + ra.rot_dim, ra.head_dim);
+  if (!(ra.theta > 1.0)) return fail(KSA_STATUS_INVALID_ARGUMENT, "theta must be > 1");
+  g_msg[0] = 0;
+  return hip_status(ksa::launch_rope(ra, x, p->dtype, static_cast<hipStream_t>(stream)), "rope");
+}
+
+int32_t ksa_rope_augmented(const ksa_params* p, int32_t batch, int64_t n_text, void* x,
+                           int32_t num_heads, int32_t head_dim, int32_t rot_off, int32_t rot_dim,
+                           double theta, void* stream) {
+  if (batch < 0 || n_text < 0) return fail(KSA_STATUS_INVALID_ARGUMENT, "negative batch/n_text");
+  if (int32_t st = check_params(p)) return st;
+  ksa::RopeArgs ra;
+  ra.batch = batch;
+  ra.rows = ksa_augmented_len(n_text, p->chunk_size);
+  ra.n_text = n_text;
+  ra.chunk = p->chunk_size;
+  ra.positions = nullptr;
+  ra.heads = num_heads;
+  ra.head_dim = head_dim;
+  ra.rot_off = rot_off;
+  ra.rot_dim = rot_dim;
+  ra.theta = theta;
+  return rope_common(p, ra, x, stream);
+}
+
+int32_t ksa_rope_positions(const ksa_params* p, int64_t rows, const int64_t* positions, void* x,
+                           int32_t num_heads, int32_t head_dim, int32_t rot_off, int32_t rot_dim,
+                           double theta, void* stream) {
+  if (rows < 0) return fail(KSA_STATUS_INVALID_ARGUMENT, "negative rows");
+  if (!positions) return fail(KSA_STATUS_INVALID_ARGUMENT, "positions is NULL");
+  if (int32_t st = check_params(p)) return st;
+  ksa::RopeArgs ra;
+  ra.batch = 1;
+  ra.rows = rows;
+  ra.n_text = 0;
+  ra.chunk = p->chunk_size;
+  ra.positions = positions;
+  ra.heads = num_heads;
+  ra.head_dim = head_dim;
+  ra.rot_off = rot_off;
+  ra.rot_dim = rot_dim;
+  ra.theta = theta;
+  return rope_common(p, ra, x, stream);
+}
+
+int32_t ksa_prefill_attn(const ksa_params* p, int32_t batch, int64_t n_text, const void* q,
+                         const void* k, const void* v, void* out, float* lse, void* stream) {
+  if (int32_t st = check_params(p)) return st;
+  if (batch < 0 || n_text < 0) return fail(KSA_STATUS_INVALID_ARGUMENT, "negative batch/n_text");
+  if (n_text > (int64_t(1) << 40)) return fail(KSA_STATUS_UNSUPPORTED, "n_text too large");
+  if (batch == 0 || n_text == 0) return KSA_STATUS_OK;
+  if (!q || !k || !out || (!p->v_is_k_prefix && !v))
+    return fail(KSA_STATUS_INVALID_ARGUMENT, "q/k/v/out pointer is NULL");
+  ksa::PrefillArgs a;
+  a.batch = batch;
+  a.n_text = n_text;
+  a.L = ksa_augmented_len(n_text, p->chunk_size);
+  a.k = p->chunk_size;
+  a.C = p->window_chunks;
+  a.hq = p->num_q_heads;
+  a.hkv = p->num_kv_heads;
+  a.dqk = p->head_dim_qk;
+  a.dv = p->head_dim_v;
+  a.v_is_k_prefix = p->v_is_k_prefix;
+  a.scale = p->softmax_scale;
+  g_msg[0] = 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (ksa::prefill_mfma_supported(a, p->dtype)) {
+    if (int32_t st = hip_status(ksa::launch_prefill_mfma_d128(a, q, k, v, out, lse, s), "prefill"))
+      return st;
+    if (a.n_text / a.k > 0)
+      return hip_status(ksa::launch_prefill_generic(a, p->dtype, 1, q, k, v, out, lse, s),
+                        "prefill summary rows");
+    return KSA_STATUS_OK;
+  }
+  return hip_status(ksa::launch_prefill_generic(a, p->dtype, 0, q, k, v, out, lse, s), "prefill");
+}
+
+int64_t ksa_cache_slots(const ksa_params* p, int32_t max_summaries) {
+  if (check_params(p) || max_summaries < 0) return -1;
+  return 1 + static_cast<int64_t>(p->chunk_size) + static_cast<int64_t>(p->window_chunks) * p->chunk_size +
+         max_summaries;
+}
+
+int32_t ksa_cache_reset(const ksa_params* p, const ksa_cache* c, int32_t batch, void* stream) {
+  if (int32_t st = check_params(p)) return st;
+  if (int32_t st = check_cache(p, c)) return st;
+  if (batch < 0) return fail(KSA_STATUS_INVALID_ARGUMENT, "negative batch");
+  if (batch == 0) return KSA_STATUS_OK;
+  g_msg[0] = 0;
+  return hip_status(ksa::launch_cache_reset(cache_args(p, c, batch), c->state,
+                                            static_cast<hipStream_t>(stream)),
+                    "cache_reset");
+}
+
+int32_t ksa_cache_append(const ksa_params* p, const ksa_cache* c, int32_t batch, const void* k_new,
+                         const void* v_new, const int32_t* kind, void* stream) {
+  if (int32_t st = check_params(p)) return st;
+  if (int32_t st = check_cache(p, c)) return st;
+  if (batch < 0) return fail(KSA_STATUS_INVALID_ARGUMENT, "negative batch");
+  if (batch == 0) return KSA_STATUS_OK;
+  if (!k_new || !kind || (!p->v_is_k_prefix && !v_new))
+    return fail(KSA_STATUS_INVALID_ARGUMENT, "k_new/v_new/kind is NULL");
+  g_msg[0] = 0;
+  return hip_status(ksa::launch_cache_append(cache_args(p, c, batch), p->dtype, c->k, c->v, c->state,
+                                             k_new, v_new, kind, static_cast<hipStream_t>(stream)),
+                    "cache_append");
+}
+
+int32_t ksa_cache_fill(const ksa_params* p, const ksa_cache* c, int32_t batch, int64_t n_text,
+                       const void* k_aug, const void* v_aug, void* stream) {
+  if (int32_t st = check_params(p)) return st;
+  if (int32_t st = check_cache(p, c)) return st;
+  if (batch < 0 || n_text < 0) return fail(KSA_STATUS_INVALID_ARGUMENT, "negative batch/n_text");
+  if (n_text / p->chunk_size > c->max_summaries)
+    return fail(KSA_STATUS_CAPACITY, "%lld complete chunks exceed max_summaries %d",
+                static_cast<long long>(n_text / p->chunk_size), c->max_summaries);
+  if (batch == 0) return KSA_STATUS_OK;
+  if (n_text > 0 && (!k_aug || (!p->v_is_k_prefix && !v_aug)))
+    return fail(KSA_STATUS_INVALID_ARGUMENT, "k_aug/v_aug is NULL");
+  g_msg[0] = 0;
+  return hip_status(ksa::launch_cache_fill(cache_args(p, c, batch), p->dtype, n_text, c->k, c->v,
+                                           c->state, k_aug, v_aug, static_cast<hipStream_t>(stream)),
+                    "cache_fill");
+}
+
+size_t ksa_decode_workspace_bytes(const ksa_params* p, int32_t batch, int32_t max_summaries) {
+  if (check_params(p) || batch < 0 || max_summaries < 0) return 0;
+  return ksa::decode_workspace_bytes(decode_args(p, batch, max_summaries));
+}
+
+int32_t ksa_decode_attn(const ksa_params* p, const ksa_cache* c, int32_t batch, const void* q,
+                        const int32_t* kind, void* out, float* lse, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  if (int32_t st = check_params(p)) return st;
+  if (int32_t st = check_cache(p, c)) return st;
+  if (batch < 0) return fail(KSA_STATUS_INVALID_ARGUMENT, "negative batch");
+  if (batch == 0) return KSA_STATUS_OK;
+  if (!q || !kind || !out) return fail(KSA_STATUS_INVALID_ARGUMENT, "q/kind/out is NULL");
+  const ksa::DecodeArgs a = decode_args(p, batch, c->max_summaries);
+  const size_t need = ksa::decode_workspace_bytes(a);
+  if (workspace_bytes < need || (need > 0 && !workspace))
+    return fail(KSA_STATUS_WORKSPACE_TOO_SMALL, "decode needs %zu workspace bytes, got %zu", need,
+                workspace_bytes);
+  g_msg[0] = 0;
+  return hip_status(ksa::launch_decode(a, p->dtype, c->k, c->v, c->state, q, kind, out, lse, workspace,
+                                       static_cast<hipStream_t>(stream)),
+                    "decode");
+}
+
+int32_t ksa_cache_read_errors(const ksa_params* p, const ksa_cache* c, int32_t batch,
+                              int32_t* host_error_bits, void* stream) {
+  if (int32_t st = check_params(p)) return st;
+  if (int32_t st = check_cache(p, c)) return st;
+  if (batch < 0 || (batch > 0 && !host_error_bits))
+    return fail(KSA_STATUS_INVALID_ARGUMENT, "bad batch or host buffer");
+  if (batch == 0) return KSA_STATUS_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (int32_t st = hip_status(hipStreamSynchronize(s), "cache_read_errors")) return st;
+  return hip_status(hipMemcpy2D(host_error_bits, sizeof(int32_t), c->state + 3, 4 * sizeof(int32_t),
+                                sizeof(int32_t), batch, hipMemcpyDeviceToHost),
+                    "cache_read_errors");
+}
+
+}  // extern "C"

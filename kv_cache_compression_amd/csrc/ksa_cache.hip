@@ -1,0 +1,190 @@
+// KSA decode cache maintenance: reset, per-step append and bulk fill.
+//
+// "Kwai Summary Attention Technical Report", Sec. 2.3.1 and Fig. 4.  The
+// cache of one (sequence, kv head) is one run of slots,
+//   [scratch | current chunk (k) | sliding-chunk ring (C*k) | summary buffer],
+// so that every decode read is a single contiguous slice (Fig. 4a).  Text
+// keys/values enter the next free current-chunk slot, right to left (4b).
+// When the chunk is complete its summary's KV goes to the scratch slot (4c),
+// the chunk is copied block-wise over the oldest ring chunk (4d) and the
+// summary is appended to the buffer (4e).
+#include "ksa_common.h"
+#include "ksa_internal.h"
+
+namespace ksa {
+
+// Copy one row of `words` 4-byte units with the whole block.
+__device__ __forceinline__ void copy_row(uint32_t* __restrict__ dst,
+                                         const uint32_t* __restrict__ src, int words) {
+  for (int w = threadIdx.x; w < words; w += blockDim.x) dst[w] = src[w];
+}
+
+__global__ void cache_reset_kernel(int32_t* state, int32_t batch) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < batch) {
+    state[4 * b + 0] = 0;
+    state[4 * b + 1] = 0;
+    state[4 * b + 2] = 0;
+    state[4 * b + 3] = 0;
+  }
+}
+
+// One block per sequence.  Words are 4-byte units of a K or V row.
+__global__ void __launch_bounds__(256) cache_append_kernel(CacheArgs a, int kw, int vw,
+                                                           uint32_t* __restrict__ ck,
+                                                           uint32_t* __restrict__ cv,
+                                                           int32_t* __restrict__ state,
+                                                           const uint32_t* __restrict__ k_new,
+                                                           const uint32_t* __restrict__ v_new,
+                                                           const int32_t* __restrict__ kind) {
+  const int b = blockIdx.x;
+  const int kd = kind[b];
+  if (kd < 0) return;
+  const int32_t m = state[4 * b + 0];
+  const int32_t r = state[4 * b + 1];
+  int err = 0;
+  if (kd == 0 && r >= a.k) err = KSA_CACHE_ERR_CHUNK_FULL;
+  if (kd != 0 && r != a.k) err = KSA_CACHE_ERR_CHUNK_NOT_FULL;
+  if (kd != 0 && err == 0 && m >= a.max_summaries) err = KSA_CACHE_ERR_SUMMARY_FULL;
+  __syncthreads();  // every thread has read the old state
+  if (err) {
+    if (threadIdx.x == 0) state[4 * b + 3] |= err;
+    return;
+  }
+  const int64_t kslot = kw, vslot = vw;  // words per slot
+  for (int h = 0; h < a.hkv; ++h) {
+    const int64_t seq = static_cast<int64_t>(b) * a.hkv + h;
+    uint32_t* kc = ck + seq * a.slots * kslot;
+    uint32_t* vc = cv ? cv + seq * a.slots * vslot : nullptr;
+    const uint32_t* kn = k_new + seq * kslot;
+    const uint32_t* vn = v_new ? v_new + seq * vslot : nullptr;
+    if (kd == 0) {
+      const int64_t slot = a.k - r;  // current chunk fills right to left
+      copy_row(kc + slot * kslot, kn, kw);
+      if (vc) copy_row(vc + slot * vslot, vn, vw);
+    } else {
+      copy_row(kc, kn, kw);  // scratch slot 0 (Fig. 4c)
+      if (vc) copy_row(vc, vn, vw);
+      if (a.C > 0) {         // finished chunk over the oldest ring chunk (Fig. 4d)
+        const int64_t dst = 1 + a.k + static_cast<int64_t>(m % a.C) * a.k;
+        for (int p = 0; p < a.k; ++p) {
+          copy_row(kc + (dst + p) * kslot, kc + (1 + p) * kslot, kw);
+          if (vc) copy_row(vc + (dst + p) * vslot, vc + (1 + p) * vslot, vw);
+        }
+      }
+      const int64_t sdst = 1 + a.k + static_cast<int64_t>(a.C) * a.k + m;  // Fig. 4e
+      copy_row(kc + sdst * kslot, kn, kw);
+      if (vc) copy_row(vc + sdst * vslot, vn, vw);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    if (kd == 0) {
+      state[4 * b + 1] = r + 1;
+    } else {
+      state[4 * b + 0] = m + 1;
+      state[4 * b + 1] = 0;
+    }
+  }
+}
+
+// Source augmented row of destination slot `slot` after n text tokens were
+// appended one by one (with every summary), or -1 if that slot was never
+// written.  M = n / k complete chunks, rem = n % k trailing tokens.
+__device__ __forceinline__ int64_t fill_source_row(int64_t slot, int64_t M, int64_t rem,
+                                                   int32_t k, int32_t C) {
+  if (slot == 0) return M >= 1 ? summary_row(M - 1, k) : -1;
+  if (slot <= k) {
+    const int64_t p = k - slot;  // token offset inside its chunk
+    if (p < rem) return text_row(M * k + p, k);
+    return M >= 1 ? text_row((M - 1) * k + p, k) : -1;
+  }
+  const int64_t ring_end = 1 + k + static_cast<int64_t>(C) * k;
+  if (slot < ring_end) {
+    const int64_t q = (slot - 1 - k) / k;        // ring chunk slot
+    const int64_t pp = (slot - 1 - k) - q * k;   // position inside it
+    if (M - 1 < q) return -1;
+    const int64_t j = q + C * ((M - 1 - q) / C); // last chunk copied there
+    return text_row(j * k + (k - 1 - pp), k);
+  }
+  const int64_t j = slot - ring_end;
+  return j < M ? summary_row(j, k) : -1;
+}
+
+__global__ void __launch_bounds__(256) cache_fill_kernel(CacheArgs a, int kw, int vw, int64_t n_text,
+                                                         uint32_t* __restrict__ ck,
+                                                         uint32_t* __restrict__ cv,
+                                                         const uint32_t* __restrict__ k_aug,
+                                                         const uint32_t* __restrict__ v_aug) {
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int64_t M = n_text / a.k;
+  const int64_t rem = n_text - M * a.k;
+  const int64_t L = n_text + M;
+  const int64_t seq = static_cast<int64_t>(b) * a.hkv + h;
+  const int64_t slots_per_block = 8;
+  const int64_t s0 = static_cast<int64_t>(blockIdx.x) * slots_per_block;
+  const int64_t nwrite = 1 + a.k + static_cast<int64_t>(a.C) * a.k + M;
+  for (int64_t slot = s0; slot < s0 + slots_per_block && slot < nwrite; ++slot) {
+    const int64_t row = fill_source_row(slot, M, rem, a.k, a.C);
+    if (row < 0) continue;
+    const int64_t src = (static_cast<int64_t>(b) * L + row) * a.hkv + h;
+    copy_row(ck + (seq * a.slots + slot) * kw, k_aug + src * kw, kw);
+    if (cv) copy_row(cv + (seq * a.slots + slot) * vw, v_aug + src * vw, vw);
+  }
+}
+
+__global__ void cache_fill_state_kernel(int32_t* state, int32_t batch, int64_t n_text, int32_t k) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < batch) {
+    state[4 * b + 0] = static_cast<int32_t>(n_text / k);
+    state[4 * b + 1] = static_cast<int32_t>(n_text % k);
+    state[4 * b + 2] = 0;
+    state[4 * b + 3] = 0;
+  }
+}
+
+static int words_per_row(int d, int32_t dtype) {
+  return dtype == KSA_DTYPE_FP32 ? d : d / 2;
+}
+
+hipError_t launch_cache_reset(const CacheArgs& a, int32_t* state, hipStream_t s) {
+  hipLaunchKernelGGL(cache_reset_kernel, dim3((a.batch + 255) / 256), dim3(256), 0, s, state,
+                     a.batch);
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_append(const CacheArgs& a, int32_t dtype, void* ck, void* cv,
+                               int32_t* state, const void* k_new, const void* v_new,
+                               const int32_t* kind, hipStream_t s) {
+  const int kw = words_per_row(a.dqk, dtype);
+  const int vw = words_per_row(a.dv, dtype);
+  const bool has_v = !a.v_is_k_prefix;
+  hipLaunchKernelGGL(cache_append_kernel, dim3(a.batch), dim3(256), 0, s, a, kw, vw,
+                     static_cast<uint32_t*>(ck), has_v ? static_cast<uint32_t*>(cv) : nullptr,
+                     state, static_cast<const uint32_t*>(k_new),
+                     has_v ? static_cast<const uint32_t*>(v_new) : nullptr, kind);
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_fill(const CacheArgs& a, int32_t dtype, int64_t n_text, void* ck, void* cv,
+                             int32_t* state, const void* k_aug, const void* v_aug, hipStream_t s) {
+  const int kw = words_per_row(a.dqk, dtype);
+  const int vw = words_per_row(a.dv, dtype);
+  const bool has_v = !a.v_is_k_prefix;
+  const int64_t M = n_text / a.k;
+  const int64_t nwrite = 1 + a.k + static_cast<int64_t>(a.C) * a.k + M;
+  const int64_t gx = (nwrite + 7) / 8;
+  hipLaunchKernelGGL(cache_fill_kernel, dim3(static_cast<uint32_t>(gx), a.hkv, a.batch), dim3(128),
+                     0, s, a, kw, vw, n_text, static_cast<uint32_t*>(ck),
+                     has_v ? static_cast<uint32_t*>(cv) : nullptr,
+                     static_cast<const uint32_t*>(k_aug),
+                     has_v ? static_cast<const uint32_t*>(v_aug) : nullptr);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(cache_fill_state_kernel, dim3((a.batch + 255) / 256), dim3(256), 0, s, state,
+                     a.batch, n_text, a.k);
+  return hipGetLastError();
+}
+
+}  // namespace ksa

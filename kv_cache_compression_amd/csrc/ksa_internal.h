@@ -1,0 +1,69 @@
+// Host-side launch functions of the KSA kernels.  Each returns hipSuccess or
+// the launch error; argument validation happens in the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/ksa.h"
+
+namespace ksa {
+
+struct RopeArgs {
+  int32_t batch;
+  int64_t rows;          // rows per batch entry
+  int64_t n_text;        // augmented rule (positions == nullptr)
+  int32_t chunk;         // k
+  const int64_t* positions;  // explicit positions [batch*rows] or nullptr
+  int32_t heads, head_dim, rot_off, rot_dim;
+  double theta;
+};
+
+hipError_t launch_rope(const RopeArgs& a, void* x, int32_t dtype, hipStream_t s);
+
+struct PrefillArgs {
+  int32_t batch;
+  int64_t n_text, L;
+  int32_t k, C, hq, hkv, dqk, dv;
+  int32_t v_is_k_prefix;
+  float scale;
+};
+
+// Generic prefill over a subset of augmented rows: rows_kind selects
+// 0 = every row, 1 = summary rows only.
+hipError_t launch_prefill_generic(const PrefillArgs& a, int32_t dtype, int rows_kind, const void* q,
+                                  const void* k, const void* v, void* out, float* lse,
+                                  hipStream_t s);
+// bf16 MFMA prefill of all text rows, Dqk = Dv = 128.
+hipError_t launch_prefill_mfma_d128(const PrefillArgs& a, const void* q, const void* k,
+                                    const void* v, void* out, float* lse, hipStream_t s);
+bool prefill_mfma_supported(const PrefillArgs& a, int32_t dtype);
+
+struct CacheArgs {
+  int32_t batch, k, C, hkv, dqk, dv;
+  int32_t v_is_k_prefix;
+  int64_t slots;
+  int32_t max_summaries;
+};
+
+hipError_t launch_cache_reset(const CacheArgs& a, int32_t* state, hipStream_t s);
+hipError_t launch_cache_append(const CacheArgs& a, int32_t dtype, void* ck, void* cv,
+                               int32_t* state, const void* k_new, const void* v_new,
+                               const int32_t* kind, hipStream_t s);
+hipError_t launch_cache_fill(const CacheArgs& a, int32_t dtype, int64_t n_text, void* ck, void* cv,
+                             int32_t* state, const void* k_aug, const void* v_aug, hipStream_t s);
+
+struct DecodeArgs {
+  int32_t batch, k, C, hq, hkv, dqk, dv;
+  int32_t v_is_k_prefix;
+  int64_t slots;
+  int32_t max_summaries;
+  float scale;
+};
+
+size_t decode_workspace_bytes(const DecodeArgs& a);
+hipError_t launch_decode(const DecodeArgs& a, int32_t dtype, const void* ck, const void* cv,
+                         const int32_t* state, const void* q, const int32_t* kind, void* out,
+                         float* lse, void* ws, hipStream_t s);
+
+}  // namespace ksa

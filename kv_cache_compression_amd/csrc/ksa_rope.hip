@@ -1,0 +1,66 @@
+// Half-split rotary embedding with the KSA position rule.
+//
+// "Kwai Summary Attention Technical Report", Sec. 2.2.1: text tokens keep
+// their text index as position id (summaries consume none) and a summary
+// token takes the id of its chunk's last text token.  RoPE is applied to Q
+// and K before attention and before keys enter the cache (Sec. 2.3.1).
+//
+// One thread owns one rotation pair (f, f + rot_dim/2) of one row and walks
+// every head of that row, so the fp64 angle and its sine/cosine are formed
+// once per (row, f).
+#include "ksa_common.h"
+#include "ksa_internal.h"
+
+namespace ksa {
+
+// Position id of augmented row a for n text tokens and chunk size k.
+__device__ __forceinline__ int64_t augmented_position(int64_t a, int64_t n, int32_t k) {
+  const int64_t M = n / k;
+  if (a < M * (k + 1)) {
+    const int64_t c = a / (k + 1);
+    const int64_t o = a - c * (k + 1);
+    return c * k + (o < k ? o : k - 1);  // summary: the chunk's last text position
+  }
+  return M * k + (a - M * (k + 1));  // trailing partial chunk
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) rope_kernel(RopeArgs a, T* __restrict__ x) {
+  const int32_t half = a.rot_dim / 2;
+  const int64_t tid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t total = static_cast<int64_t>(a.batch) * a.rows * half;
+  if (tid >= total) return;
+  const int32_t f = static_cast<int32_t>(tid % half);
+  const int64_t br = tid / half;  // batch * rows + row
+  const int64_t row = br % a.rows;
+  const int64_t pos = a.positions ? a.positions[br] : augmented_position(row, a.n_text, a.chunk);
+  const double inv_freq = pow(a.theta, -2.0 * static_cast<double>(f) / a.rot_dim);
+  const double ang = static_cast<double>(pos) * inv_freq;
+  double sn, cs;
+  sincos(ang, &sn, &cs);
+  T* base = x + br * a.heads * static_cast<int64_t>(a.head_dim) + a.rot_off + f;
+  for (int32_t h = 0; h < a.heads; ++h) {
+    T* p = base + static_cast<int64_t>(h) * a.head_dim;
+    const double lo = load_f32(p);
+    const double hi = load_f32(p + half);
+    store_f32(p, static_cast<float>(lo * cs - hi * sn));
+    store_f32(p + half, static_cast<float>(hi * cs + lo * sn));
+  }
+}
+
+hipError_t launch_rope(const RopeArgs& a, void* x, int32_t dtype, hipStream_t s) {
+  const int64_t total = static_cast<int64_t>(a.batch) * a.rows * (a.rot_dim / 2);
+  if (total == 0) return hipSuccess;
+  const int threads = 256;
+  const int64_t blocks = (total + threads - 1) / threads;
+  if (dtype == KSA_DTYPE_FP32) {
+    hipLaunchKernelGGL(rope_kernel<float>, dim3(static_cast<uint32_t>(blocks)), dim3(threads), 0, s,
+                       a, static_cast<float*>(x));
+  } else {
+    hipLaunchKernelGGL(rope_kernel<bf16_t>, dim3(static_cast<uint32_t>(blocks)), dim3(threads), 0,
+                       s, a, static_cast<bf16_t*>(x));
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ksa

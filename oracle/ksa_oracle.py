@@ -461,6 +461,30 @@ class CacheModel:
         return out
 
 
+def slot_of_row(a: int, m: int, r: int, k: int, C: int) -> int:
+    """Physical slot that holds augmented row ``a`` in cache state (m, r).
+
+    Follows the placement rules of :class:`CacheModel` (Fig. 4): summary s_j
+    at buffer position j; text token p of a committed chunk c in the window
+    at ring chunk-slot (c mod C), position k-1-p (the current chunk is copied
+    block-wise and fills right to left); token p of the current chunk at
+    current-chunk slot k-1-p.  Raises if the row is not held.
+    """
+    n_guess = a + 1
+    kind, idx = decode_row(a, n_guess + k * 2, k)
+    cur0, ring0, sum0 = 1, 1 + k, 1 + k + C * k
+    if kind == "s":
+        if idx >= m:
+            raise KeyError(a)
+        return sum0 + idx
+    c, p = divmod(idx, k)
+    if c == m and p < r:
+        return cur0 + k - 1 - p
+    if max(0, m - C) <= c < m and C > 0:
+        return ring0 + (c % C) * k + (k - 1 - p)
+    raise KeyError(a)
+
+
 def cache_held_rows(m: int, r: int, k: int, C: int) -> List[int]:
     """Augmented rows a cache must hold in state (m committed chunks, r tokens
     in the current chunk): every committed summary, the text of the last

@@ -1,0 +1,113 @@
+"""Host-side checks of the C ABI library (no GPU needed).
+
+The library must load, export every function ``include/ksa.h`` declares, and
+reject bad arguments on the host, before anything is launched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import kv_cache_compression_amd as K
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(K.LIB_PATH):
+        from kv_cache_compression_amd import _build
+        _build.build()
+    return K.lib()
+
+
+def _declared():
+    txt = open(os.path.join(ROOT, "include", "ksa.h")).read()
+    return sorted(set(re.findall(r"KSA_API[^;(]*?\b(ksa_\w+)\s*\(", txt)))
+
+
+def test_exports_every_declared_symbol(L):
+    decl = _declared()
+    assert len(decl) == 13
+    assert sorted(K.EXPORTS) == decl
+    for name in decl:
+        assert hasattr(L, name), name
+
+
+def _params(**kw):
+    d = dict(chunk_size=8, window_chunks=4, num_q_heads=4, num_kv_heads=2, head_dim_qk=64,
+             head_dim_v=64, v_is_k_prefix=0, softmax_scale=0.125, dtype=K.KSA_DTYPE_FP32)
+    d.update(kw)
+    return K.ksa_params(**d)
+
+
+def test_sizes(L):
+    assert L.ksa_augmented_len(512, 8) == 576
+    assert L.ksa_augmented_len(517, 8) == 581
+    assert L.ksa_augmented_len(-1, 8) == -1
+    assert L.ksa_augmented_len(5, 0) == -1
+    p = _params()
+    assert L.ksa_cache_slots(ctypes.byref(p), 100) == 1 + 8 + 32 + 100
+    assert L.ksa_cache_slots(ctypes.byref(p), -1) == -1
+    assert L.ksa_decode_workspace_bytes(ctypes.byref(p), 64, 16384) > 0
+
+
+def _status(L, rc):
+    return rc, L.ksa_last_error_message().decode()
+
+
+def test_invalid_arguments_rejected_before_launch(L):
+    p = _params()
+    fake = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    rc, msg = _status(L, L.ksa_prefill_attn(None, 1, 512, fake, fake, fake, fake, None, None))
+    assert rc == 1 and "NULL" in msg
+    bad = _params(num_q_heads=3)
+    rc, msg = _status(L, L.ksa_prefill_attn(ctypes.byref(bad), 1, 512, fake, fake, fake, fake, None, None))
+    assert rc == 1 and "multiple" in msg
+    bad = _params(dtype=7)
+    rc, _ = _status(L, L.ksa_prefill_attn(ctypes.byref(bad), 1, 512, fake, fake, fake, fake, None, None))
+    assert rc == 2
+    bad = _params(chunk_size=0)
+    rc, _ = _status(L, L.ksa_prefill_attn(ctypes.byref(bad), 1, 512, fake, fake, fake, fake, None, None))
+    assert rc == 1
+    bad = _params(softmax_scale=0.0)
+    rc, _ = _status(L, L.ksa_prefill_attn(ctypes.byref(bad), 1, 512, fake, fake, fake, fake, None, None))
+    assert rc == 1
+    rc, _ = _status(L, L.ksa_prefill_attn(ctypes.byref(p), 1, 512, fake, fake, None, fake, None, None))
+    assert rc == 1  # v missing without v_is_k_prefix
+    bad = _params(head_dim_qk=64, head_dim_v=128, v_is_k_prefix=1)
+    rc, _ = _status(L, L.ksa_prefill_attn(ctypes.byref(bad), 1, 512, fake, fake, None, fake, None, None))
+    assert rc == 1
+    assert L.ksa_prefill_attn(ctypes.byref(p), 0, 512, None, None, None, None, None, None) == 0
+
+
+def test_cache_argument_checks(L):
+    p = _params()
+    fake = ctypes.c_void_p(16)
+    c = K.ksa_cache(16, 16, 16, 10)
+    # 11 complete chunks do not fit in a 10-summary buffer
+    rc, msg = _status(L, L.ksa_cache_fill(ctypes.byref(p), ctypes.byref(c), 1, 88, fake, fake, None))
+    assert rc == 3 and "max_summaries" in msg
+    rc, _ = _status(L, L.ksa_cache_append(ctypes.byref(p), None, 1, fake, fake, fake, None))
+    assert rc == 1
+    rc, _ = _status(L, L.ksa_decode_attn(ctypes.byref(p), ctypes.byref(c), 2, fake, fake, fake, None,
+                                         fake, 8, None))
+    assert rc == 4
+    nov = K.ksa_cache(16, None, 16, 10)
+    rc, _ = _status(L, L.ksa_cache_append(ctypes.byref(p), ctypes.byref(nov), 1, fake, fake, fake, None))
+    assert rc == 1
+
+
+def test_status_strings(L):
+    assert L.ksa_status_string(0) == b"ok"
+    assert L.ksa_status_string(4) == b"workspace too small"
+    assert L.ksa_status_string(99) == b"unknown status"
+
+
+def test_python_binding_requires_gpu_tensors(L):
+    p = K.Params(8, 4, 4, 2, 64, 64, torch.float32)
+    q = torch.zeros(1, 576, 4, 64)
+    with pytest.raises(ValueError):
+        K.ksa_prefill_attn(p, q, torch.zeros(1, 576, 2, 64), torch.zeros(1, 576, 2, 64), 512)

@@ -80,3 +80,12 @@ def test_cache_slots_per_token_tend_to_table1():
     mla = slots * (dc + dr) / n / (2 * h * d)
     assert abs(gqa - 1 / k * g / h) < 1e-5
     assert abs(mla - 1 / k * (dc + dr) / (2 * h * d)) < 1e-5
+
+
+@pytest.mark.parametrize("k,C", [(4, 2), (8, 3), (3, 1), (1, 2), (4, 0)])
+def test_slot_of_row_matches_model(k, C):
+    for kind, n_text, cm in _run(k, C, 60, 60):
+        for slot_payload in cm.held():
+            a = slot_payload
+            s = O.slot_of_row(a, cm.m, cm.r, k, C)
+            assert cm.slots[s] == a
