@@ -39,6 +39,7 @@ constexpr int ROW_BYTES = D * 2;  // 256 B per key row
 constexpr int TILE_BYTES = BN * ROW_BYTES;
 
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // 16-byte chunk c (0..15) of LDS row `row` is stored at chunk c ^ swz(row):
 // 8 consecutive rows hit 8 different even chunks, and the next 8 the odd
@@ -146,11 +147,11 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_d128_kernel(
   const int64_t kv_row_stride = static_cast<int64_t>(a.hkv) * D;  // elements per augmented row
   const bf16_t* kb = kx + static_cast<int64_t>(b) * a.L * kv_row_stride + kvh * D + 8 * ld_chunk;
   const bf16_t* vb = vx + static_cast<int64_t>(b) * a.L * kv_row_stride + kvh * D + 8 * ld_chunk;
-  uint4 kreg[4], vreg[4];
+  u32x4_t kreg[4], vreg[4];
   const int n_total = runs.ns + runs.nt;
 
+  // Augmented row of key r of tile tt, clamped inside its run.
   auto tile_key_row = [&](int tt, int r) -> int64_t {
-    // augmented row of key r of tile tt (clamped inside its run)
     if (tt < runs.ns) {
       int64_t j = static_cast<int64_t>(tt) * BN + r;
       if (j >= runs.sn) j = runs.sn - 1;
@@ -160,14 +161,14 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_d128_kernel(
     if (t > runs.t1) t = runs.t1;
     return text_row(t, a.k);
   };
-  auto prefetch = [&](int tt) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t ar = tile_key_row(tt, ld_row + 16 * u);
-      kreg[u] = *reinterpret_cast<const uint4*>(kb + ar * kv_row_stride);
-      vreg[u] = *reinterpret_cast<const uint4*>(vb + ar * kv_row_stride);
-    }
-  };
+#define KSA_PREFETCH(tt)                                                        \
+  do {                                                                          \
+    _Pragma("unroll") for (int u = 0; u < 4; ++u) {                             \
+      const int64_t ar = tile_key_row((tt), ld_row + 16 * u);                   \
+      kreg[u] = *reinterpret_cast<const u32x4_t*>(kb + ar * kv_row_stride);    \
+      vreg[u] = *reinterpret_cast<const u32x4_t*>(vb + ar * kv_row_stride);    \
+    }                                                                           \
+  } while (0)
 
   f32x16_t oacc[4];
 #pragma unroll
@@ -178,17 +179,17 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_d128_kernel(
   float l_run = 0.f;
   const float sl = a.scale * kLog2e;
 
-  if (n_total > 0) prefetch(0);
+  if (n_total > 0) KSA_PREFETCH(0);
   for (int tt = 0; tt < n_total; ++tt) {
     __syncthreads();  // everyone is done with the previous tile
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int r = ld_row + 16 * u;
-      *reinterpret_cast<uint4*>(k_lds + lds_off(r, ld_chunk)) = kreg[u];
-      *reinterpret_cast<uint4*>(v_lds + lds_off(r, ld_chunk)) = vreg[u];
+      *reinterpret_cast<u32x4_t*>(k_lds + lds_off(r, ld_chunk)) = kreg[u];
+      *reinterpret_cast<u32x4_t*>(v_lds + lds_off(r, ld_chunk)) = vreg[u];
     }
     __syncthreads();
-    if (tt + 1 < n_total) prefetch(tt + 1);
+    if (tt + 1 < n_total) KSA_PREFETCH(tt + 1);
 
     // Does this tile hold anything for this wave, and does it need a mask?
     const bool is_sum = tt < runs.ns;
@@ -277,6 +278,7 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_d128_kernel(
     }
   }
 
+#undef KSA_PREFETCH
   if (!wave_active) return;
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (!q_valid) return;
