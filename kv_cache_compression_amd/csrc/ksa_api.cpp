@@ -184,14 +184,8 @@ int32_t ksa_prefill_attn(const ksa_params* p, int32_t batch, int64_t n_text, con
   a.scale = p->softmax_scale;
   g_msg[0] = 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (ksa::prefill_mfma_supported(a, p->dtype)) {
-    if (int32_t st = hip_status(ksa::launch_prefill_mfma_d128(a, q, k, v, out, lse, s), "prefill"))
-      return st;
-    if (a.n_text / a.k > 0)
-      return hip_status(ksa::launch_prefill_generic(a, p->dtype, 1, q, k, v, out, lse, s),
-                        "prefill summary rows");
-    return KSA_STATUS_OK;
-  }
+  if (ksa::prefill_mfma_supported(a, p->dtype))
+    return hip_status(ksa::launch_prefill_mfma_d128(a, q, k, v, out, lse, s), "prefill");
   return hip_status(ksa::launch_prefill_generic(a, p->dtype, 0, q, k, v, out, lse, s), "prefill");
 }
 

@@ -4,28 +4,33 @@
 // splits Q/K/V into fixed-size blocks and loads only block pairs that hold
 // visible entries; the O(L^2) mask is never built.  The visible set of text
 // token t_i (chunk c = floor(i/k)) is, by Eq. (3), the summaries
-// s_0 .. s_{c-C-1} and the text t_{(c-C)k} .. t_i.  So for a block of
-// consecutive text queries the visible keys are two runs, each contiguous in
-// its own index space: a summary run [0, c_last - C) and a text run
-// [(c_first - C) k, i_last].  This kernel walks those two runs in 64-key
+// s_0 .. s_{c-C-1} and the text t_{(c-C)k} .. t_i.  For a block of
+// consecutive text queries the visible keys are therefore two runs, each
+// contiguous in its own index space: a summary run [0, c_last - C) and a
+// text run [(c_first - C) k, i_last].  The kernel walks those runs in 64-key
 // tiles; only tiles on a run's edge need an element mask, computed from
-// integer compares on chunk indices.  Summary-query rows (k+1 keys each) are
-// handled by the generic kernel.
+// integer compares on chunk indices.  A summary query s_j reads only its own
+// chunk's k text tokens and itself (Sec. 2.2.1), i.e. the k+1 consecutive
+// augmented rows j(k+1) .. j(k+1)+k; those rows are handled by extra
+// workgroups at the end of the same launch.
 //
-// Work decomposition (one workgroup = 4 wavefronts):
+// Text workgroups (4 wavefronts, 256 threads):
 //   - a workgroup owns one kv head and HPW of its query heads over PT
 //     consecutive text positions (HPW * PT = 128 query rows); every wave owns
-//     32 query rows of one head, so the K/V tile staged in LDS feeds 4 waves;
-//   - S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q
-//     held in registers), so each lane ends up owning one query row and the
-//     softmax row statistics stay in-lane (one lane swap per tile);
-//   - O^T += V^T P^T on the same MFMA: P goes straight from the score
-//     registers into the B operand; V^T comes from the row-major V tile via
-//     ds_read_b64_tr_b16 (transposing 4x16 bf16 blocks per 16 lanes);
-//   - K/V tiles are prefetched into registers one tile ahead;
-//   - workgroups are ordered longest-first (later queries see more
-//     summaries) and, when the head count allows, all workgroups of one
-//     (sequence, kv head) run on one XCD so its K/V stay in that XCD's L2.
+//     32 query rows of one head, so each K/V tile staged in LDS feeds 4 waves;
+//   - S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q in
+//     registers): each lane owns one query row, so the softmax statistics
+//     stay in-lane apart from one swap with the lane 32 away;
+//   - O^T += V^T P^T on the same MFMA: P goes from the score registers into
+//     the B operand; V^T comes from the row-major V tile through
+//     ds_read_b64_tr_b16 (4x16 bf16 transposes within each 16 lanes);
+//   - the running maximum is only moved (and O rescaled) when a tile's
+//     maximum exceeds it by more than 2^8, which keeps every exponent <= 8;
+//   - K/V tiles are double-buffered in LDS and prefetched one tile ahead
+//     into registers: one barrier per tile;
+//   - workgroups run longest-first (later queries see more summaries) and,
+//     when the head count allows, all workgroups of one (sequence, kv head)
+//     sit on one XCD so that its K/V stay in that XCD's L2.
 #include "ksa_common.h"
 #include "ksa_internal.h"
 
@@ -37,137 +42,231 @@ constexpr int D = 128;
 constexpr int BN = 64;            // keys per tile
 constexpr int ROW_BYTES = D * 2;  // 256 B per key row
 constexpr int TILE_BYTES = BN * ROW_BYTES;
+constexpr float kLazyRescale = 8.f;  // log2 units
 
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+
+struct MfmaArgs {
+  int32_t batch, n, L, k, C, hq, hkv, g, M;
+  int32_t n_tiles, n_hg, xcd_map, n_text_blocks;
+  uint32_t divk_m, divk_l;  // floor(t / k) = (umulhi(t, m) + t) >> l for t < 2^31
+  float sl;                 // softmax scale * log2(e)
+};
+
+__device__ __forceinline__ int32_t div_k(const MfmaArgs& a, int32_t t) {
+  return static_cast<int32_t>((__umulhi(static_cast<uint32_t>(t), a.divk_m) + static_cast<uint32_t>(t)) >>
+                              a.divk_l);
+}
+__device__ __forceinline__ int32_t trow(const MfmaArgs& a, int32_t t) { return t + div_k(a, t); }
+__device__ __forceinline__ int32_t srow(const MfmaArgs& a, int32_t j) { return j * (a.k + 1) + a.k; }
 
 // 16-byte chunk c (0..15) of LDS row `row` is stored at chunk c ^ swz(row):
-// 8 consecutive rows hit 8 different even chunks, and the next 8 the odd
-// ones, so the MFMA operand reads of 32 rows x 16 B and the transposing
-// reads of 4 rows x 32 B are spread over all banks.
+// 8 consecutive rows hit 8 different even chunks and the next 8 the odd
+// ones, so MFMA operand reads (32 rows x 16 B) and transposing reads
+// (4 rows x 32 B per 16 lanes) spread over the banks.
 __device__ __forceinline__ int lds_off(int row, int chunk) {
   const int swz = ((row & 7) << 1) | ((row >> 3) & 1);
   return row * ROW_BYTES + ((chunk ^ swz) << 4);
 }
 
-typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
-
-__device__ __forceinline__ bf16x4_t lds_read_tr(const char* lds_base, int byte_off) {
-  const lds_bf16x4_t* p = (const lds_bf16x4_t*)((__attribute__((address_space(3))) char*)(lds_base) + byte_off);
-  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(const_cast<lds_bf16x4_t*>(p));
+__device__ __forceinline__ bf16x4_t lds_read_tr(const char* base, int byte_off) {
+  auto p = (lds_bf16x4_t*)((__attribute__((address_space(3))) char*)(base) + byte_off);
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p);
 }
 
-struct TileRuns {
-  int64_t sn;   // summaries visible to the block: s_0 .. s_{sn-1}
-  int64_t t0;   // first text key
-  int64_t t1;   // last text key (inclusive)
-  int ns, nt;   // summary tiles, text tiles
-};
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+}
 
-__device__ __forceinline__ TileRuns block_runs(int64_t p_first, int64_t p_last, int32_t k,
-                                               int32_t C) {
-  TileRuns r;
-  const int64_t c_first = p_first / k;
-  const int64_t c_last = p_last / k;
-  r.sn = c_last - C > 0 ? c_last - C : 0;
-  r.t0 = c_first - C > 0 ? (c_first - C) * k : 0;
-  r.t1 = p_last;
-  r.ns = static_cast<int>((r.sn + BN - 1) / BN);
-  r.nt = static_cast<int>((r.t1 - r.t0 + 1 + BN - 1) / BN);
-  return r;
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Summary query rows: one wave per (sequence, kv head, summary j); it
+// attends every query head of the group to the k+1 rows j(k+1) .. j(k+1)+k.
+// Lanes: 16 per key row (8 bf16 of d each), 4 rows per pass.
+__device__ void summary_rows_wave(const MfmaArgs& a, int64_t item, const bf16_t* __restrict__ q,
+                                  const bf16_t* __restrict__ kx, const bf16_t* __restrict__ vx,
+                                  bf16_t* __restrict__ out, float* __restrict__ lse) {
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 15;    // d chunk: d = 8 c .. 8 c + 7
+  const int grp = lane >> 4;  // row slot within a pass
+  const int j = static_cast<int>(item % a.M);
+  const int kvh = static_cast<int>((item / a.M) % a.hkv);
+  const int b = static_cast<int>(item / (static_cast<int64_t>(a.M) * a.hkv));
+  const int r0 = j * (a.k + 1);
+  const int nrows = a.k + 1;
+  const int64_t kvs = static_cast<int64_t>(a.hkv) * D;
+  const bf16_t* kb = kx + static_cast<int64_t>(b) * a.L * kvs + kvh * D + 8 * c;
+  const bf16_t* vb = vx + static_cast<int64_t>(b) * a.L * kvs + kvh * D + 8 * c;
+  const int srow_a = r0 + a.k;  // the summary's own augmented row
+  for (int hh = 0; hh < a.g; ++hh) {
+    const int h = kvh * a.g + hh;
+    const u32x4_t qw = *reinterpret_cast<const u32x4_t*>(
+        q + (static_cast<int64_t>(b) * a.L + srow_a) * a.hq * D + static_cast<int64_t>(h) * D + 8 * c);
+    const float qf[8] = {bf_lo(qw.x), bf_hi(qw.x), bf_lo(qw.y), bf_hi(qw.y),
+                         bf_lo(qw.z), bf_hi(qw.z), bf_lo(qw.w), bf_hi(qw.w)};
+    float m = kNegInf, l = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < nrows; s0 += 4) {
+      const int slot = s0 + grp;
+      const bool ok = slot < nrows;
+      const int row = r0 + (ok ? slot : 0);
+      const u32x4_t kw = *reinterpret_cast<const u32x4_t*>(kb + row * kvs);
+      float part = qf[0] * bf_lo(kw.x) + qf[1] * bf_hi(kw.x) + qf[2] * bf_lo(kw.y) +
+                   qf[3] * bf_hi(kw.y) + qf[4] * bf_lo(kw.z) + qf[5] * bf_hi(kw.z) +
+                   qf[6] * bf_lo(kw.w) + qf[7] * bf_hi(kw.w);
+      part += __shfl_xor(part, 8);
+      part += __shfl_xor(part, 4);
+      part += __shfl_xor(part, 2);
+      part += __shfl_xor(part, 1);
+      const float s = ok ? part * a.sl : kNegInf;
+      const float mn = fmaxf(m, s);
+      const float mu = mn == kNegInf ? 0.f : mn;
+      const float al = fast_exp2(m - mu);
+      const float p = fast_exp2(s - mu);
+      const u32x4_t vw = *reinterpret_cast<const u32x4_t*>(vb + row * kvs);
+      const float vf[8] = {bf_lo(vw.x), bf_hi(vw.x), bf_lo(vw.y), bf_hi(vw.y),
+                           bf_lo(vw.z), bf_hi(vw.z), bf_lo(vw.w), bf_hi(vw.w)};
+      l = l * al + p;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = o[e] * al + p * vf[e];
+      m = mn;
+    }
+    // merge the four row slots (lane groups 16 apart); a group that saw no
+    // row (k + 1 < 4) carries m = -inf and contributes nothing
+    float mx = fmaxf(m, __shfl_xor(m, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float w = m == kNegInf ? 0.f : fast_exp2(m - mx);
+    l *= w;
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x = o[e] * w;
+      x += __shfl_xor(x, 16);
+      x += __shfl_xor(x, 32);
+      o[e] = x;
+    }
+    if (grp == 0) {
+      const float inv = 1.f / l;
+      u32x4_t ow;
+      ow.x = pk_bf16(o[0] * inv, o[1] * inv);
+      ow.y = pk_bf16(o[2] * inv, o[3] * inv);
+      ow.z = pk_bf16(o[4] * inv, o[5] * inv);
+      ow.w = pk_bf16(o[6] * inv, o[7] * inv);
+      *reinterpret_cast<u32x4_t*>(out + (static_cast<int64_t>(b) * a.L + srow_a) * a.hq * D +
+                                  static_cast<int64_t>(h) * D + 8 * c) = ow;
+      if (lse && c == 0)
+        lse[(static_cast<int64_t>(b) * a.hq + h) * a.L + srow_a] = (mx + log2f(l)) * kLn2;
+    }
+  }
 }
 
 }  // namespace
 
 template <int HPW>
 __global__ void __launch_bounds__(256, 2) prefill_mfma_d128_kernel(
-    PrefillArgs a, int n_tiles, int n_hg, int xcd_map, const bf16_t* __restrict__ q,
-    const bf16_t* __restrict__ kx, const bf16_t* __restrict__ vx, bf16_t* __restrict__ out,
-    float* __restrict__ lse) {
+    MfmaArgs a, const bf16_t* __restrict__ q, const bf16_t* __restrict__ kx,
+    const bf16_t* __restrict__ vx, bf16_t* __restrict__ out, float* __restrict__ lse) {
   constexpr int PT = 32 * (4 / HPW);  // text positions per workgroup
-  __shared__ __attribute__((aligned(16))) char k_lds[TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) char v_lds[TILE_BYTES];
-
-  const int g = a.hq / a.hkv;
-  const int64_t n_slots = static_cast<int64_t>(a.batch) * a.hkv * n_hg;
-  const int64_t bid = blockIdx.x;
-  int64_t hslot, t_rev;
-  if (xcd_map) {  // blocks are dispatched round-robin over the 8 XCDs
-    const int64_t x = bid & 7, s = bid >> 3;
-    hslot = (s / n_tiles) * 8 + x;
-    t_rev = s % n_tiles;
-  } else {
-    hslot = bid % n_slots;
-    t_rev = bid / n_slots;
-  }
-  const int tile = n_tiles - 1 - static_cast<int>(t_rev);  // longest first
-  const int hg = static_cast<int>(hslot % n_hg);
-  const int kvh = static_cast<int>((hslot / n_hg) % a.hkv);
-  const int b = static_cast<int>(hslot / (static_cast<int64_t>(n_hg) * a.hkv));
+  __shared__ __attribute__((aligned(16))) char lds[2][2][TILE_BYTES];  // [buffer][K, V]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int h = kvh * g + hg * HPW + (wave % HPW);
-  const int64_t p0 = static_cast<int64_t>(tile) * PT;
-  const int64_t p_last = (p0 + PT < a.n_text ? p0 + PT : a.n_text) - 1;
-  const TileRuns runs = block_runs(p0, p_last, a.k, a.C);
+  if (static_cast<int>(blockIdx.x) >= a.n_text_blocks) {
+    const int64_t item = static_cast<int64_t>(blockIdx.x - a.n_text_blocks) * 4 + wave;
+    if (item < static_cast<int64_t>(a.batch) * a.hkv * a.M) summary_rows_wave(a, item, q, kx, vx, out, lse);
+    return;
+  }
+
+  const int n_slots = a.batch * a.hkv * a.n_hg;
+  const int bid = blockIdx.x;
+  int hslot, t_rev;
+  if (a.xcd_map) {  // blocks are dispatched round-robin over the 8 XCDs
+    const int x = bid & 7, s = bid >> 3;
+    hslot = (s / a.n_tiles) * 8 + x;
+    t_rev = s % a.n_tiles;
+  } else {
+    hslot = bid % n_slots;
+    t_rev = bid / n_slots;
+  }
+  const int tile = a.n_tiles - 1 - t_rev;  // longest first
+  const int hg = hslot % a.n_hg;
+  const int kvh = (hslot / a.n_hg) % a.hkv;
+  const int b = hslot / (a.n_hg * a.hkv);
+  const int h = kvh * a.g + hg * HPW + (wave % HPW);
+
+  // Key runs of the workgroup.
+  const int p0 = tile * PT;
+  const int p_last = (p0 + PT < a.n ? p0 + PT : a.n) - 1;
+  const int c_first = div_k(a, p0), c_last = div_k(a, p_last);
+  const int sn = c_last - a.C > 0 ? c_last - a.C : 0;           // summaries s_0 .. s_{sn-1}
+  const int t0 = c_first - a.C > 0 ? (c_first - a.C) * a.k : 0;  // text t0 .. p_last
+  const int ns = (sn + BN - 1) / BN;
+  const int n_total = ns + (p_last - t0 + BN) / BN;
 
   // This wave's 32 queries and this lane's query.
-  const int64_t iw0 = p0 + 32 * (wave / HPW);
-  const int64_t iw1 = (iw0 + 31 < a.n_text ? iw0 + 31 : a.n_text - 1);
-  const bool wave_active = iw0 < a.n_text;
-  const int64_t qi = iw0 + (lane & 31);
-  const bool q_valid = qi < a.n_text;
-  const int64_t ci = qi / a.k;
-  const int64_t smax = q_valid ? ci - a.C - 1 : -1;  // visible summaries: j <= smax
-  const int64_t tlo = q_valid ? (ci - a.C > 0 ? (ci - a.C) * a.k : 0) : INT64_MAX;
-  const int64_t thi = qi;
-  const int64_t cw0 = iw0 / a.k, cw1 = iw1 / a.k;
-  const int64_t tlo_w1 = cw1 - a.C > 0 ? (cw1 - a.C) * a.k : 0;
-  const int64_t tlo_w0 = cw0 - a.C > 0 ? (cw0 - a.C) * a.k : 0;
+  const int iw0 = p0 + 32 * (wave / HPW);
+  const int iw1 = iw0 + 31 < a.n ? iw0 + 31 : a.n - 1;
+  const bool wave_active = iw0 < a.n;
+  const int qi = iw0 + (lane & 31);
+  const bool q_valid = qi < a.n;
+  const int ci = div_k(a, q_valid ? qi : 0);
+  const int smax = q_valid ? ci - a.C - 1 : -1;                       // summaries j <= smax
+  const int tlo = q_valid ? (ci - a.C > 0 ? (ci - a.C) * a.k : 0) : 0x7fffffff;
+  const int thi = qi;
+  const int cw0 = div_k(a, wave_active ? iw0 : 0), cw1 = div_k(a, wave_active ? iw1 : 0);
+  const int tlo_w0 = cw0 - a.C > 0 ? (cw0 - a.C) * a.k : 0;
+  const int tlo_w1 = cw1 - a.C > 0 ? (cw1 - a.C) * a.k : 0;
 
   // Q^T as the B operand: column = query (lane % 32), k-slots
   // d = 16 ks + 8 (lane / 32) + j.
   const int half = lane >> 5;
   bf16x8_t qop[8];
   {
-    const int64_t qrow = text_row(q_valid ? qi : 0, a.k);
-    const bf16_t* qp = q + ((static_cast<int64_t>(b) * a.L + qrow) * a.hq + h) * D + 8 * half;
+    const int qrow = trow(a, q_valid ? qi : 0);
+    const bf16_t* qp =
+        q + (static_cast<int64_t>(b) * a.L + qrow) * a.hq * D + static_cast<int64_t>(h) * D + 8 * half;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
+    for (int ks = 0; ks < 8; ++ks)
       qop[ks] = q_valid ? *reinterpret_cast<const bf16x8_t*>(qp + 16 * ks) : bf16x8_t{};
-    }
   }
 
-  // Global -> register prefetch of one K and one V tile: thread owns chunk
-  // (tid % 16) of rows tid/16 + 16 u.
+  // Global -> register prefetch of one K and one V tile: thread owns 16-byte
+  // chunk (tid % 16) of rows tid/16 + 16 u.
   const int ld_chunk = tid & 15;
   const int ld_row = tid >> 4;
-  const int64_t kv_row_stride = static_cast<int64_t>(a.hkv) * D;  // elements per augmented row
-  const bf16_t* kb = kx + static_cast<int64_t>(b) * a.L * kv_row_stride + kvh * D + 8 * ld_chunk;
-  const bf16_t* vb = vx + static_cast<int64_t>(b) * a.L * kv_row_stride + kvh * D + 8 * ld_chunk;
+  const int kvs = a.hkv * D;  // elements per augmented row
+  const bf16_t* kb = kx + static_cast<int64_t>(b) * a.L * kvs + kvh * D + 8 * ld_chunk;
+  const bf16_t* vb = vx + static_cast<int64_t>(b) * a.L * kvs + kvh * D + 8 * ld_chunk;
   u32x4_t kreg[4], vreg[4];
-  const int n_total = runs.ns + runs.nt;
-
-  // Augmented row of key r of tile tt, clamped inside its run.
-  auto tile_key_row = [&](int tt, int r) -> int64_t {
-    if (tt < runs.ns) {
-      int64_t j = static_cast<int64_t>(tt) * BN + r;
-      if (j >= runs.sn) j = runs.sn - 1;
-      return summary_row(j, a.k);
-    }
-    int64_t t = runs.t0 + static_cast<int64_t>(tt - runs.ns) * BN + r;
-    if (t > runs.t1) t = runs.t1;
-    return text_row(t, a.k);
-  };
-#define KSA_PREFETCH(tt)                                                        \
-  do {                                                                          \
-    _Pragma("unroll") for (int u = 0; u < 4; ++u) {                             \
-      const int64_t ar = tile_key_row((tt), ld_row + 16 * u);                   \
-      kreg[u] = *reinterpret_cast<const u32x4_t*>(kb + ar * kv_row_stride);    \
-      vreg[u] = *reinterpret_cast<const u32x4_t*>(vb + ar * kv_row_stride);    \
-    }                                                                           \
+#define KSA_PREFETCH(tt)                                                          \
+  do {                                                                            \
+    _Pragma("unroll") for (int u = 0; u < 4; ++u) {                               \
+      const int r_ = ld_row + 16 * u;                                             \
+      int ar_;                                                                    \
+      if ((tt) < ns) {                                                            \
+        const int j_ = (tt) * BN + r_;                                            \
+        ar_ = srow(a, j_ < sn ? j_ : sn - 1);                                     \
+      } else {                                                                    \
+        const int t_ = t0 + ((tt) - ns) * BN + r_;                                \
+        ar_ = trow(a, t_ < p_last ? t_ : p_last);                                 \
+      }                                                                           \
+      kreg[u] = *reinterpret_cast<const u32x4_t*>(kb + ar_ * kvs);                \
+      vreg[u] = *reinterpret_cast<const u32x4_t*>(vb + ar_ * kvs);                \
+    }                                                                             \
+  } while (0)
+#define KSA_STORE(buf)                                                            \
+  do {                                                                            \
+    _Pragma("unroll") for (int u = 0; u < 4; ++u) {                               \
+      const int off_ = lds_off(ld_row + 16 * u, ld_chunk);                        \
+      *reinterpret_cast<u32x4_t*>(&lds[buf][0][off_]) = kreg[u];                  \
+      *reinterpret_cast<u32x4_t*>(&lds[buf][1][off_]) = vreg[u];                  \
+    }                                                                             \
   } while (0)
 
   f32x16_t oacc[4];
@@ -175,26 +274,28 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_d128_kernel(
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  float m_run = kNegInf;
-  float l_run = 0.f;
-  const float sl = a.scale * kLog2e;
+  float m_ref = kNegInf;  // reference maximum (log2 units), shared by lanes i and i^32
+  float l_run = 0.f;      // this lane's half of the row sum
 
-  if (n_total > 0) KSA_PREFETCH(0);
+  // transposing-read coordinates (see the P.V step)
+  const int G = lane >> 4;
+  const int l16 = lane & 15;
+  const int rr = l16 >> 2, c4 = l16 & 3;
+
+  if (n_total > 0) {
+    KSA_PREFETCH(0);
+    KSA_STORE(0);
+  }
+  __syncthreads();
   for (int tt = 0; tt < n_total; ++tt) {
-    __syncthreads();  // everyone is done with the previous tile
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int r = ld_row + 16 * u;
-      *reinterpret_cast<u32x4_t*>(k_lds + lds_off(r, ld_chunk)) = kreg[u];
-      *reinterpret_cast<u32x4_t*>(v_lds + lds_off(r, ld_chunk)) = vreg[u];
-    }
-    __syncthreads();
+    const int cur = tt & 1;
     if (tt + 1 < n_total) KSA_PREFETCH(tt + 1);
+    const char* kl = lds[cur][0];
+    const char* vl = lds[cur][1];
 
     // Does this tile hold anything for this wave, and does it need a mask?
-    const bool is_sum = tt < runs.ns;
-    const int64_t key0 = is_sum ? static_cast<int64_t>(tt) * BN
-                                : runs.t0 + static_cast<int64_t>(tt - runs.ns) * BN;
+    const bool is_sum = tt < ns;
+    const int key0 = is_sum ? tt * BN : t0 + (tt - ns) * BN;
     bool empty, full;
     if (is_sum) {
       empty = key0 > cw1 - a.C - 1;
@@ -203,123 +304,152 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_d128_kernel(
       empty = key0 > iw1 || key0 + BN - 1 < tlo_w0;
       full = key0 >= tlo_w1 && key0 + BN - 1 <= iw0;
     }
-    if (!wave_active || empty) continue;
-
-    // ---- S^T = K Q^T: two 32-key blocks ----
-    f32x16_t sacc[2];
+    if (wave_active && !empty) {
+      // ---- S^T = K Q^T: two 32-key blocks ----
+      f32x16_t sacc[2];
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kb2][r] = 0.f;
-      const int krow = 32 * kb2 + (lane & 31);
+        for (int r = 0; r < 16; ++r) sacc[kb2][r] = 0.f;
+        const int krow = 32 * kb2 + (lane & 31);
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8_t kop =
-            *reinterpret_cast<const bf16x8_t*>(k_lds + lds_off(krow, 2 * ks + half));
-        sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[ks], sacc[kb2], 0, 0, 0);
-      }
-    }
-
-    // ---- online softmax; lane = query, registers = keys ----
-    // key of (kb2, r) = 32 kb2 + 8 (r / 4) + 4 half + r % 4
-    float tmax = kNegInf;
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float s = sacc[kb2][r] * sl;
-        if (!full) {
-          const int64_t key = key0 + 32 * kb2 + 8 * (r >> 2) + 4 * half + (r & 3);
-          const bool vis = is_sum ? key <= smax : (key >= tlo && key <= thi);
-          s = vis ? s : kNegInf;
+        for (int ks = 0; ks < 8; ++ks) {
+          const bf16x8_t kop = *reinterpret_cast<const bf16x8_t*>(kl + lds_off(krow, 2 * ks + half));
+          sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[ks], sacc[kb2], 0, 0, 0);
         }
-        sacc[kb2][r] = s;
-        tmax = fmaxf(tmax, s);
       }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
-    const float m_use = m_new == kNegInf ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    m_run = m_new;
-    float psum = 0.f;
-    bf16x8_t pop[4];
+      // ---- mask (edge tiles only) and tile maximum of the raw scores ----
+      // key of (kb2, r) = key0 + 32 kb2 + 8 (r / 4) + 4 half + r % 4
+      if (!full) {
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
+        for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(sacc[kb2][r] - m_use);
-        psum += p;
-        pop[2 * kb2 + (r >> 3)][r & 7] = static_cast<__bf16>(p);
+          for (int r = 0; r < 16; ++r) {
+            const int key = key0 + 32 * kb2 + 8 * (r >> 2) + 4 * half + (r & 3);
+            const bool vis = is_sum ? key <= smax : (key >= tlo && key <= thi);
+            sacc[kb2][r] = vis ? sacc[kb2][r] : kNegInf;
+          }
       }
-    l_run = l_run * alpha + psum;
+      float tmax = kNegInf;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+      for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-
-    // ---- O^T += V^T P^T ----
-    // Transposing read: in 16-lane group G, lane (4 rr + c4) points at key
-    // row 16 ks + 8 rd + 4 (G / 2) + rr, d = 32 db + 16 (G % 2) + 4 c4; lane
-    // then receives V[4 keys][d = 32 db + lane % 32].
-    const int G = lane >> 4;
-    const int l16 = lane & 15;
-    const int rr = l16 >> 2, c4 = l16 & 3;
+        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sacc[kb2][r]);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * a.sl;
+      // ---- lazy move of the reference maximum ----
+      const bool grow = tmax > m_ref + kLazyRescale;
+      if (__any(grow)) {
+        const float m_new = fmaxf(m_ref, tmax);
+        const float alpha = m_ref == kNegInf ? 0.f : fast_exp2(m_ref - m_new);
+        m_ref = m_new;
+        l_run *= alpha;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+        for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const int d = 32 * db + 16 * (G & 1) + 4 * c4;
-        const int row0 = 16 * ks + 4 * (G >> 1) + rr;
-        const bf16x4_t lo = lds_read_tr(v_lds, lds_off(row0, d >> 3) + 2 * (d & 7));
-        const bf16x4_t hi = lds_read_tr(v_lds, lds_off(row0 + 8, d >> 3) + 2 * (d & 7));
-        const bf16x8_t vop = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[ks], oacc[db], 0, 0, 0);
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      }
+      const float nm = m_ref == kNegInf ? 0.f : -m_ref;
+      // ---- P = exp2(s * sl - m), packed to bf16 B operands ----
+      u32x4_t pw[4];
+      float psum = 0.f;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float p0f = fast_exp2(fmaf(sacc[kb2][r], a.sl, nm));
+          const float p1f = fast_exp2(fmaf(sacc[kb2][r + 1], a.sl, nm));
+          psum += p0f + p1f;
+          pw[2 * kb2 + (r >> 3)][(r & 7) >> 1] = pk_bf16(p0f, p1f);
+        }
+      l_run += psum;
+      // ---- O^T += V^T P^T ----
+      // Transposing read: in 16-lane group G, lane (4 rr + c4) points at key
+      // row 16 ks + 8 rd + 4 (G / 2) + rr, d = 32 db + 16 (G % 2) + 4 c4, and
+      // receives V[4 keys][d = 32 db + lane % 32].
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, pw[ks]);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const int d = 32 * db + 16 * (G & 1) + 4 * c4;
+          const int row0 = 16 * ks + 4 * (G >> 1) + rr;
+          const bf16x4_t lo = lds_read_tr(vl, lds_off(row0, d >> 3) + 2 * (d & 7));
+          const bf16x4_t hi = lds_read_tr(vl, lds_off(row0 + 8, d >> 3) + 2 * (d & 7));
+          const bf16x8_t vop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop, oacc[db], 0, 0, 0);
+        }
       }
     }
+    if (tt + 1 < n_total) KSA_STORE(cur ^ 1);
+    __syncthreads();
   }
-
 #undef KSA_PREFETCH
+#undef KSA_STORE
+
   if (!wave_active) return;
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (!q_valid) return;
   const float inv = 1.f / l_tot;
-  const int64_t orow = text_row(qi, a.k);
-  bf16_t* op = out + ((static_cast<int64_t>(b) * a.L + orow) * a.hq + h) * D;
+  const int orow = trow(a, qi);
+  bf16_t* op = out + (static_cast<int64_t>(b) * a.L + orow) * a.hq * D + static_cast<int64_t>(h) * D;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
       const int d = 32 * db + 8 * qq + 4 * half;
       uint2 w;
-      w.x = pack_bf16x2(oacc[db][4 * qq + 0] * inv, oacc[db][4 * qq + 1] * inv);
-      w.y = pack_bf16x2(oacc[db][4 * qq + 2] * inv, oacc[db][4 * qq + 3] * inv);
+      w.x = pk_bf16(oacc[db][4 * qq + 0] * inv, oacc[db][4 * qq + 1] * inv);
+      w.y = pk_bf16(oacc[db][4 * qq + 2] * inv, oacc[db][4 * qq + 3] * inv);
       *reinterpret_cast<uint2*>(op + d) = w;
     }
   if (lse && half == 0)
-    lse[(static_cast<int64_t>(b) * a.hq + h) * a.L + orow] = (m_run + log2f(l_tot)) * kLn2;
+    lse[(static_cast<int64_t>(b) * a.hq + h) * a.L + orow] = (m_ref + log2f(l_tot)) * kLn2;
 }
 
 bool prefill_mfma_supported(const PrefillArgs& a, int32_t dtype) {
   const int g = a.hq / a.hkv;
-  return dtype == KSA_DTYPE_BF16 && a.dqk == D && a.dv == D && !a.v_is_k_prefix &&
+  // 32-bit index arithmetic inside the kernel
+  const bool fits = a.L < (int64_t(1) << 30) &&
+                    a.L * static_cast<int64_t>(a.hq > a.hkv ? a.hq : a.hkv) * D < (int64_t(1) << 31) &&
+                    static_cast<int64_t>(a.batch) * a.hkv * g * ((a.n_text + 31) / 32) < (int64_t(1) << 31);
+  return dtype == KSA_DTYPE_BF16 && a.dqk == D && a.dv == D && !a.v_is_k_prefix && fits &&
          (g == 1 || g == 2 || g % 4 == 0);
 }
 
+static void fast_div(uint32_t d, uint32_t* m, uint32_t* l) {
+  uint32_t s = 0;
+  while ((uint64_t(1) << s) < d) ++s;
+  *l = s;
+  *m = static_cast<uint32_t>(((uint64_t(1) << 32) * ((uint64_t(1) << s) - d)) / d + 1);
+}
+
 template <int HPW>
-static hipError_t launch_hpw(const PrefillArgs& a, const void* q, const void* k, const void* v,
+static hipError_t launch_hpw(const PrefillArgs& p, const void* q, const void* k, const void* v,
                              void* out, float* lse, hipStream_t s) {
   constexpr int PT = 32 * (4 / HPW);
-  const int g = a.hq / a.hkv;
-  const int n_hg = g / HPW;
-  const int n_tiles = static_cast<int>((a.n_text + PT - 1) / PT);
-  const int64_t n_slots = static_cast<int64_t>(a.batch) * a.hkv * n_hg;
-  const int64_t blocks = n_slots * n_tiles;
+  MfmaArgs a;
+  a.batch = p.batch;
+  a.n = static_cast<int32_t>(p.n_text);
+  a.L = static_cast<int32_t>(p.L);
+  a.k = p.k;
+  a.C = p.C;
+  a.hq = p.hq;
+  a.hkv = p.hkv;
+  a.g = p.hq / p.hkv;
+  a.M = static_cast<int32_t>(p.n_text / p.k);
+  a.n_hg = a.g / HPW;
+  a.n_tiles = static_cast<int32_t>((p.n_text + PT - 1) / PT);
+  const int64_t n_slots = static_cast<int64_t>(a.batch) * a.hkv * a.n_hg;
+  a.n_text_blocks = static_cast<int32_t>(n_slots * a.n_tiles);
+  a.xcd_map = (n_slots % 8) == 0 ? 1 : 0;
+  fast_div(static_cast<uint32_t>(a.k), &a.divk_m, &a.divk_l);
+  a.sl = p.scale * kLog2e;
+  const int64_t sum_items = static_cast<int64_t>(a.batch) * a.hkv * a.M;
+  const int64_t blocks = a.n_text_blocks + (sum_items + 3) / 4;
   if (blocks == 0) return hipSuccess;
-  const int xcd_map = (n_slots % 8) == 0 ? 1 : 0;
   hipLaunchKernelGGL(prefill_mfma_d128_kernel<HPW>, dim3(static_cast<uint32_t>(blocks)), dim3(256),
-                     0, s, a, n_tiles, n_hg, xcd_map, static_cast<const bf16_t*>(q),
-                     static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v),
-                     static_cast<bf16_t*>(out), lse);
+                     0, s, a, static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
+                     static_cast<const bf16_t*>(v), static_cast<bf16_t*>(out), lse);
   return hipGetLastError();
 }
 
