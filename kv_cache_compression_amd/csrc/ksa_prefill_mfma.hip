@@ -31,6 +31,8 @@
 //   - workgroups run longest-first (later queries see more summaries) and,
 //     when the head count allows, all workgroups of one (sequence, kv head)
 //     sit on one XCD so that its K/V stay in that XCD's L2.
+#include <type_traits>
+
 #include "ksa_common.h"
 #include "ksa_internal.h"
 
@@ -277,18 +279,30 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_d128_kernel(
   float m_ref = kNegInf;  // reference maximum (log2 units), shared by lanes i and i^32
   float l_run = 0.f;      // this lane's half of the row sum
 
-  // transposing-read coordinates (see the P.V step)
-  const int G = lane >> 4;
-  const int l16 = lane & 15;
-  const int rr = l16 >> 2, c4 = l16 & 3;
-
-  if (n_total > 0) {
-    KSA_PREFETCH(0);
-    KSA_STORE(0);
+  // Per-lane LDS byte offsets, fixed for the whole loop (tile rows and
+  // buffers only add constants).  K operand: row lane % 32 (+32), chunk
+  // 2 ks + half.  Transposing V reads: in 16-lane group G, lane (4 rr + c4)
+  // points at key row 16 ks + 8 rd + 4 (G / 2) + rr and d = 32 db + 16 (G % 2)
+  // + 4 c4, and receives V[4 keys][d = 32 db + lane % 32].
+  int koff[8], voff[2][4];
+  {
+    const int G = lane >> 4, l16 = lane & 15, rr = l16 >> 2, c4 = l16 & 3;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) koff[ks] = lds_off(lane & 31, 2 * ks + half);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int d = 32 * db + 16 * (G & 1) + 4 * c4;
+      const int row0 = 4 * (G >> 1) + rr;
+      voff[0][db] = lds_off(row0, d >> 3) + 2 * (d & 7);
+      voff[1][db] = lds_off(row0 + 8, d >> 3) + 2 * (d & 7);
+    }
   }
-  __syncthreads();
-  for (int tt = 0; tt < n_total; ++tt) {
-    const int cur = tt & 1;
+  const uint32_t one2 = 0x3f803f80u;  // two bf16 ones
+
+  // One tile: `cur` is a compile-time buffer index so LDS addresses fold
+  // into instruction offsets.
+  auto tile_step = [&](auto cur_c, int tt) {
+    constexpr int cur = decltype(cur_c)::value;
     if (tt + 1 < n_total) KSA_PREFETCH(tt + 1);
     const char* kl = lds[cur][0];
     const char* vl = lds[cur][1];
@@ -311,23 +325,24 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_d128_kernel(
       for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[kb2][r] = 0.f;
-        const int krow = 32 * kb2 + (lane & 31);
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
-          const bf16x8_t kop = *reinterpret_cast<const bf16x8_t*>(kl + lds_off(krow, 2 * ks + half));
+          const bf16x8_t kop = *reinterpret_cast<const bf16x8_t*>(kl + koff[ks] + 32 * ROW_BYTES * kb2);
           sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[ks], sacc[kb2], 0, 0, 0);
         }
       }
-      // ---- mask (edge tiles only) and tile maximum of the raw scores ----
+      // ---- mask (edge tiles only): visible iff lo <= key <= hi ----
       // key of (kb2, r) = key0 + 32 kb2 + 8 (r / 4) + 4 half + r % 4
       if (!full) {
+        const int lo = is_sum ? -1 : tlo;
+        const int hi = is_sum ? smax : thi;
+        const int kbase = key0 + 4 * half;
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int key = key0 + 32 * kb2 + 8 * (r >> 2) + 4 * half + (r & 3);
-            const bool vis = is_sum ? key <= smax : (key >= tlo && key <= thi);
-            sacc[kb2][r] = vis ? sacc[kb2][r] : kNegInf;
+            const int key = kbase + 32 * kb2 + 8 * (r >> 2) + (r & 3);
+            sacc[kb2][r] = (key >= lo && key <= hi) ? sacc[kb2][r] : kNegInf;
           }
       }
       float tmax = kNegInf;
@@ -349,32 +364,28 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_d128_kernel(
           for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
       }
       const float nm = m_ref == kNegInf ? 0.f : -m_ref;
-      // ---- P = exp2(s * sl - m), packed to bf16 B operands ----
+      // ---- P = exp2(s * sl - m) in bf16; the row sum adds the same
+      //      rounded values that multiply V ----
       u32x4_t pw[4];
-      float psum = 0.f;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
           const float p0f = fast_exp2(fmaf(sacc[kb2][r], a.sl, nm));
           const float p1f = fast_exp2(fmaf(sacc[kb2][r + 1], a.sl, nm));
-          psum += p0f + p1f;
-          pw[2 * kb2 + (r >> 3)][(r & 7) >> 1] = pk_bf16(p0f, p1f);
+          const uint32_t w = pk_bf16(p0f, p1f);
+          pw[2 * kb2 + (r >> 3)][(r & 7) >> 1] = w;
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w),
+                                                  __builtin_bit_cast(bf16x2_t, one2), l_run, false);
         }
-      l_run += psum;
       // ---- O^T += V^T P^T ----
-      // Transposing read: in 16-lane group G, lane (4 rr + c4) points at key
-      // row 16 ks + 8 rd + 4 (G / 2) + rr, d = 32 db + 16 (G % 2) + 4 c4, and
-      // receives V[4 keys][d = 32 db + lane % 32].
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, pw[ks]);
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-          const int d = 32 * db + 16 * (G & 1) + 4 * c4;
-          const int row0 = 16 * ks + 4 * (G >> 1) + rr;
-          const bf16x4_t lo = lds_read_tr(vl, lds_off(row0, d >> 3) + 2 * (d & 7));
-          const bf16x4_t hi = lds_read_tr(vl, lds_off(row0 + 8, d >> 3) + 2 * (d & 7));
+          const bf16x4_t lo = lds_read_tr(vl, voff[0][db] + 16 * ROW_BYTES * ks);
+          const bf16x4_t hi = lds_read_tr(vl, voff[1][db] + 16 * ROW_BYTES * ks);
           const bf16x8_t vop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop, oacc[db], 0, 0, 0);
         }
@@ -382,6 +393,16 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_d128_kernel(
     }
     if (tt + 1 < n_total) KSA_STORE(cur ^ 1);
     __syncthreads();
+  };
+
+  if (n_total > 0) {
+    KSA_PREFETCH(0);
+    KSA_STORE(0);
+  }
+  __syncthreads();
+  for (int tt = 0; tt < n_total; tt += 2) {
+    tile_step(std::integral_constant<int, 0>(), tt);
+    if (tt + 1 < n_total) tile_step(std::integral_constant<int, 1>(), tt + 1);
   }
 #undef KSA_PREFETCH
 #undef KSA_STORE
