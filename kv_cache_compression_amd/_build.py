@@ -19,6 +19,7 @@ SOURCES = [
     "ksa_prefill_mfma.hip",
     "ksa_cache.hip",
     "ksa_decode.hip",
+    "ksa_decode_mla.hip",
 ]
 
 # Packed fp32 ops stay disabled for every kernel.

@@ -349,7 +349,9 @@ static int choose_splits(const DecodeArgs& a) {
 }
 
 size_t decode_workspace_bytes(const DecodeArgs& a) {
-  return static_cast<size_t>(a.batch) * a.hq * kDecMaxSplits * (a.dv + 2) * sizeof(float);
+  // sized for either split-K path; the generic path needs none
+  const size_t gqa = static_cast<size_t>(a.batch) * a.hq * kDecMaxSplits * (a.dv + 2) * sizeof(float);
+  return a.v_is_k_prefix ? decode_mla_workspace_bytes(a) : gqa;
 }
 
 template <int G>
@@ -366,6 +368,13 @@ hipError_t launch_decode(const DecodeArgs& a, int32_t dtype, const void* ck, con
                          const int32_t* state, const void* q, const int32_t* kind, void* out,
                          float* lse, void* ws, hipStream_t s) {
   int32_t* st = const_cast<int32_t*>(state);
+  if (decode_mla_supported(a, dtype)) {
+    hipLaunchKernelGGL(decode_check_kernel, dim3((a.batch + 255) / 256), dim3(256), 0, s, a.batch,
+                       a.k, a.C, a.max_summaries, st, kind);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_decode_mla(a, ck, state, q, kind, out, lse, ws, s);
+  }
   if (!gqa_fast_ok(a, dtype)) {
     if (dtype == KSA_DTYPE_FP32)
       return launch_decode_generic<float>(a, ck, cv, st, q, kind, out, lse, s);

@@ -286,3 +286,70 @@ def test_full_size_gqa_decode_sampled():
 
 def test_full_size_mla_decode_sampled():
     _sampled_decode_check(ksa_synth.DECODE_MLA, [0, 9, 31])
+
+
+@pytest.mark.parametrize("k,C,n_prefix,B", [(8, 4, 700, 3), (4, 2, 93, 2), (8, 64, 3000, 2)])
+def test_mla_decode_values_vs_oracle(k, C, n_prefix, B):
+    """Absorbed-MLA shape (128 heads on one 576-wide latent head, V = first
+    512 key columns): fill, then text and summary steps, against the oracle."""
+    dev = _dev()
+    hq, D, Dv = 128, 576, 512
+    n_total = n_prefix + k + 2
+    L = O.augmented_len(n_total, k)
+    g = ksa_synth.gen(31)
+    ka = ksa_synth.normal((B, L, 1, D), torch.bfloat16, g)
+    qa = ksa_synth.normal((B, L, hq, D), torch.bfloat16, g)
+    p = ksa.Params(k, C, hq, 1, D, Dv, torch.bfloat16, v_is_k_prefix=True)
+    cache = ksa.Cache(p, B, n_total // k + 1, device=dev)
+    Lp = O.augmented_len(n_prefix, k)
+    ksa.ksa_cache_fill(cache, ka[:, :Lp].to(dev).contiguous(), None, n_prefix)
+    ws = ksa.decode_workspace(cache)
+    is_s, _ = O.augmented_rows(n_total, k)
+    n_text = n_prefix
+    for a in range(Lp, L):
+        kind = 1 if is_s[a] else 0
+        kt = torch.full((B,), kind, dtype=torch.int32, device=dev)
+        ksa.ksa_cache_append(cache, ka[:, a].to(dev).contiguous(), None, kt)
+        if not kind:
+            n_text += 1
+        lse = torch.empty((B, hq), dtype=torch.float32, device=dev)
+        out = ksa.ksa_decode_attn(cache, qa[:, a].to(dev).contiguous(), kt, lse=lse, workspace=ws)
+        torch.cuda.synchronize()
+        for b in range(B):
+            ref, rl = O.decode_attention(qa[b, a].double().numpy(), ka[b].double().numpy(), None,
+                                         n_text, k, C, p.scale, "s" if kind else "t", dv=Dv)
+            e = np.abs(_np(out[b]) - ref)
+            assert e.max() <= 2e-2 and e.mean() <= 2e-3, (a, b, e.max(), e.mean())
+            assert np.abs(_np(lse[b]) - rl).max() <= 2e-2
+    assert ksa.ksa_cache_read_errors(cache) == [0] * B
+
+
+def test_mla_decode_visibility_onehot():
+    """q = 0 and one-hot latent values: output column d > 0 exactly for the
+    rows of the oracle's mask row, at every step, text and summary."""
+    dev = _dev()
+    hq, D, Dv, k, C, n_total = 128, 576, 512, 4, 3, 150
+    L = O.augmented_len(n_total, k)
+    rk = torch.zeros((L, 1, D), dtype=torch.bfloat16)
+    g = ksa_synth.gen(8)
+    rk[:, :, Dv:] = ksa_synth.normal((L, 1, D - Dv), torch.bfloat16, g)
+    for a in range(L):
+        rk[a, :, a] = 1.0
+    p = ksa.Params(k, C, hq, 1, D, Dv, torch.bfloat16, v_is_k_prefix=True)
+    cache = ksa.Cache(p, 1, 64, device=dev)
+    q = torch.zeros((1, hq, D), dtype=torch.bfloat16, device=dev)
+    ws = ksa.decode_workspace(cache)
+    is_s, _ = O.augmented_rows(n_total, k)
+    n_text = 0
+    for a in range(L):
+        kind = 1 if is_s[a] else 0
+        kt = torch.tensor([kind], dtype=torch.int32, device=dev)
+        ksa.ksa_cache_append(cache, rk[a][None].to(dev).contiguous(), None, kt)
+        if not kind:
+            n_text += 1
+        out = ksa.ksa_decode_attn(cache, q, kt, workspace=ws)
+        torch.cuda.synchronize()
+        want = O.decode_visible_rows(n_text, k, C, "s" if kind else "t")
+        o = _np(out[0])
+        for h in (0, 37, 127):
+            np.testing.assert_array_equal(np.nonzero(o[h] > 0)[0], want, err_msg=f"row {a} head {h}")
