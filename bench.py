@@ -6,7 +6,12 @@ in HBM:
   2. KSA prefill attention (32K text tokens, k=8, w=64, 32/8 heads, d=128, bf16),
   3. hand-off of that prefill's K/V into its decode cache (bulk fill),
   4. one decode step of the 64-sequence, 131072-token-history batch
-     (text-token cache append, then split-K decode over the contiguous slice).
+     (text-token cache append, then split-K decode over the contiguous slice),
+  5. one decode step of the 32-sequence absorbed-MLA batch (ragged 16K-128K
+     histories, 128 heads on one 576/512 latent head), rotating over three
+     cache copies so that reads come from HBM.
+The 131072-token prefill (w = 64 and w = 16) is timed separately after the
+steps and reported beside them.
 
 ``value`` is the prefill throughput in TFLOP/s counted over visible
 (query, key) pairs only, 2 (Dqk + Dv) Hq per pair; the decode step's HBM
@@ -66,6 +71,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-long", action="store_true", help="skip the 131072-token prefill lines")
     ap.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0 = auto)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -126,9 +132,39 @@ def main() -> int:
         dec_rows += r + min(m, dw.window) * dw.chunk + max(0, m - dw.window)
     dec_bytes = (dec_rows * dw.hkv * (dw.dqk + dw.dv) * 2
                  + dw.batch * dw.hq * (dw.dqk + dw.dv) * 2)  # cache slice + q + out
+    # ---- absorbed-MLA decode workload: 32 sequences, ragged histories ----
+    mw = ksa_synth.DECODE_MLA
+    mp = ksa.Params(mw.chunk, mw.window, mw.hq, mw.hkv, mw.dqk, mw.dv, mw.dtype, v_is_k_prefix=True)
+    mhist = ksa_synth.decode_histories(mw)
+    mmax = max(n // mw.chunk for n in mhist) + 1
+    mcaches = []
+    for c in range(3):   # > 3 x the 256 MB last-level cache in total
+        mc = ksa.Cache(mp, mw.batch, mmax, device=dev)
+        gm = torch.Generator(device=dev)
+        gm.manual_seed(mw.seed + c)
+        mc.k.normal_(generator=gm)
+        mst = torch.zeros((mw.batch, 4), dtype=torch.int32)
+        for b, n in enumerate(mhist):
+            m = (n - 1) // mw.chunk
+            mst[b, 0] = m
+            mst[b, 1] = n - m * mw.chunk
+        mc.state.copy_(mst.to(dev))
+        mcaches.append(mc)
+    mq = ksa_synth.decode_query(mw).to(dev)
+    mkind = torch.zeros((mw.batch,), dtype=torch.int32, device=dev)
+    mout = torch.empty((mw.batch, mw.hq, mw.dv), dtype=mw.dtype, device=dev)
+    mws = ksa.decode_workspace(mcaches[0])
+    mla_rows = 0
+    for n in mhist:
+        m = (n - 1) // mw.chunk
+        r = n - m * mw.chunk
+        mla_rows += r + min(m, mw.window) * mw.chunk + max(0, m - mw.window)
+    mla_bytes = mla_rows * mw.dqk * 2 + mw.batch * mw.hq * (mw.dqk + mw.dv) * 2
+    mla_flops = 2 * mw.hq * (mw.dqk + mw.dv) * mla_rows
     torch.cuda.synchronize()
 
-    segs = ["rope", "prefill", "fill", "append", "decode"]
+    segs = ["rope", "prefill", "fill", "append", "decode", "decode_mla"]
+    counter = [0]
 
     def step(ev):
         ev[0].record(stream)
@@ -144,8 +180,12 @@ def main() -> int:
         ev[4].record(stream)
         ksa.ksa_decode_attn(dcache, dq, kind, out=dout, workspace=ws, stream=stream)
         ev[5].record(stream)
+        mc = mcaches[counter[0] % len(mcaches)]
+        counter[0] += 1
+        ksa.ksa_decode_attn(mc, mq, mkind, out=mout, workspace=mws, stream=stream)
+        ev[6].record(stream)
 
-    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(7)]
     for _ in range(args.warmup):
         step(mk())
     torch.cuda.synchronize()
@@ -156,13 +196,16 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     seg_ms = {s: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps for i, s in enumerate(segs)}
-    errs = ksa.ksa_cache_read_errors(dcache)
-    if any(errs):
-        raise RuntimeError(f"decode cache error bits {errs}")
+    for c in [dcache] + mcaches:
+        errs = ksa.ksa_cache_read_errors(c)
+        if any(errs):
+            raise RuntimeError(f"decode cache error bits {errs}")
+    long_runs = [] if args.no_long else prefill_long(ksa, ksa_synth, torch, dev, stream)
 
     pre_tflops = flops / (seg_ms["prefill"] * 1e-3) / 1e12
     dec_gbps = dec_bytes / (seg_ms["decode"] * 1e-3) / 1e9
     rope_gbps = rope_bytes / (seg_ms["rope"] * 1e-3) / 1e9
+    mla_gbps = mla_bytes / (seg_ms["decode_mla"] * 1e-3) / 1e9
 
     res = {
         "metric": METRIC,
@@ -189,6 +232,12 @@ def main() -> int:
         },
         "decode": {"value": round(dec_gbps, 1), "unit": "GB/s", "frac_of_peak": round(dec_gbps / PEAK_HBM_GBPS, 4),
                    "ms": round(seg_ms["decode"], 4)},
+        "decode_mla": {"value": round(mla_gbps, 1), "unit": "GB/s",
+                       "frac_of_peak": round(mla_gbps / PEAK_HBM_GBPS, 4),
+                       "tflops": round(mla_flops / (seg_ms["decode_mla"] * 1e-3) / 1e12, 1),
+                       "ms": round(seg_ms["decode_mla"], 4), "workload": mw.name,
+                       "slice_rows_total": mla_rows, "bytes": mla_bytes},
+        "prefill_long": long_runs,
         "rope": {"value": round(rope_gbps, 1), "unit": "GB/s", "ms": round(seg_ms["rope"], 4)},
         "breakdown_ms": {s: round(v, 4) for s, v in seg_ms.items()},
         "roofline": {"kernel": "prefill_mfma_d128_kernel", "bound": "mfma", "achieved": round(pre_tflops, 2),
@@ -199,6 +248,37 @@ def main() -> int:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
     print(json.dumps(res), flush=True)
     return 0
+
+
+def prefill_long(ksa, ksa_synth, torch, dev, stream, reps: int = 5) -> list:
+    """The 131072-token prefill at w = 64 and w = 16 (RoPE pre-pass applied
+    once, outside the timing)."""
+    res = []
+    for w in (ksa_synth.PREFILL_128K_W64, ksa_synth.PREFILL_128K_W16):
+        L = ksa.ksa_augmented_len(w.n_text, w.chunk)
+        g = ksa_synth.gen(w.seed)
+        qd = ksa_synth.normal((w.batch, L, w.hq, w.dqk), w.dtype, g).to(dev)
+        kd = ksa_synth.normal((w.batch, L, w.hkv, w.dqk), w.dtype, g).to(dev)
+        vd = ksa_synth.normal((w.batch, L, w.hkv, w.dv), w.dtype, g).to(dev)
+        p = ksa.Params(w.chunk, w.window, w.hq, w.hkv, w.dqk, w.dv, w.dtype)
+        ksa.ksa_rope_augmented(p, qd, w.n_text, w.rope_theta, stream=stream)
+        ksa.ksa_rope_augmented(p, kd, w.n_text, w.rope_theta, stream=stream)
+        out = torch.empty((w.batch, L, w.hq, w.dv), dtype=w.dtype, device=dev)
+        ksa.ksa_prefill_attn(p, qd, kd, vd, w.n_text, out=out, stream=stream)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(reps):
+            ksa.ksa_prefill_attn(p, qd, kd, vd, w.n_text, out=out, stream=stream)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / reps
+        fl = 2 * (w.dqk + w.dv) * w.hq * visible_pairs(w.n_text, w.chunk, w.window) * w.batch
+        tf = fl / (ms * 1e-3) / 1e12
+        res.append({"workload": w.name, "ms": round(ms, 4), "tflops": round(tf, 2),
+                    "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4), "flops": fl})
+        del qd, kd, vd, out
+        torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(w, rows_req: int) -> dict:

@@ -8,21 +8,25 @@
 // contiguous slice (Sec. 2.3.1, Fig. 4).
 //
 // Work decomposition: the slices of all sequences are cut into row ranges of
-// about (total rows / CU count); one workgroup of 8 wavefronts handles one
-// range for all 128 heads, so every cache row leaves HBM once.
-//   - 32-key tiles are copied global -> LDS with global_load_lds_dwordx4
-//     (no registers involved), three buffers deep; rows are padded to 1168
-//     bytes so that both the MFMA operand reads (32 rows x 16 B) and the
-//     transposing reads (4 rows x 32 B) are free of bank conflicts;
-//   - waves 2j and 2j+1 own heads 32j .. 32j+31.  Each computes half of
-//     S^T = K Q^T (key columns 0..287 or 288..575) on 32x32x16 bf16 MFMA,
-//     the halves are summed through LDS, both run the same softmax, and
-//     each accumulates half of O^T += V^T P^T (value columns 0..255 or
-//     256..511), V^T read through ds_read_b64_tr_b16 from the same tile.
-//     Splitting the key width as well as the value width keeps the MFMA
-//     work undivided while each wave holds half of Q and half of O;
+// about (total rows / CU count); two workgroups of 8 wavefronts (heads 0..63
+// and 64..127) handle one range, so every cache row leaves HBM once and is
+// read a second time from L2.
+//   - 32-key tiles are prefetched one tile ahead into registers with buffer
+//     loads (a lane past the range reads zeros) and stored to a double-
+//     buffered LDS tile; rows are padded to 1168 bytes so that both the MFMA
+//     operand reads (32 rows x 16 B) and the transposing reads (4 rows x
+//     32 B) are free of bank conflicts;
+//   - waves 4j .. 4j+3 own a block of 32 heads.  Wave 4j+u computes the
+//     part of S^T = K Q^T over key columns 144u .. 144u+143 on 32x32x16 bf16
+//     MFMA; the four parts are summed through LDS, all four run the same
+//     softmax, and wave 4j+u accumulates value columns 128u .. 128u+127 of
+//     O^T += V^T P^T, V^T read through ds_read_b64_tr_b16 from the same
+//     tile.  Splitting the key width as well as the value width keeps the
+//     MFMA work undivided while each wave holds a quarter of Q and of O;
 //   - each range writes (max, sum, unnormalised output in bf16) per head;
 //     a second kernel merges the ranges of a sequence by their maxima.
+#include <type_traits>
+
 #include "ksa_common.h"
 #include "ksa_internal.h"
 
@@ -32,13 +36,13 @@ namespace {
 
 constexpr int DQK = 576, DV = 512;
 constexpr int HQ = 128;
-constexpr int NW = 8;                     // waves per workgroup: 4 head blocks x 2 halves
+constexpr int NW = 8;                     // waves per workgroup: 2 head blocks x 4 quarters
+constexpr int HWG = 64;                   // heads per workgroup
 constexpr int TK = 32;                    // keys per tile
 constexpr int RB = DQK * 2 + 16;          // padded LDS row: 1168 bytes (73 chunks)
 constexpr int RCH = RB / 16;              // 73
 constexpr int LOADS_PER_WAVE = 5;         // 16-byte lanes: 5 x 64 x 8 = 2560 >= 32 x 73
 constexpr int TILE_LDS = NW * LOADS_PER_WAVE * 64 * 16;  // 40960 bytes
-constexpr int NBUF = 3;
 constexpr float kLazy = 8.f;
 
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
@@ -50,6 +54,14 @@ typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 
 __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+}
+
+// Workgroup barrier without a memory fence; callers wait for exactly the
+// counters they need first.
+__device__ __forceinline__ void wg_barrier() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
 }
 
 __device__ __forceinline__ bf16x4_t lds_read_tr(const char* base, int byte_off) {
@@ -85,40 +97,93 @@ __device__ __forceinline__ MlaSlice mla_slice(const MlaArgs& a, const int32_t* s
   return s;
 }
 
-// Rows per range for sequence b: about total/n_cu, at least 64, and at most
-// smax ranges per sequence.  Both kernels derive the same split from the
-// device-side cache state.
-__device__ __forceinline__ void mla_split(const MlaArgs& a, const int32_t* state, const int32_t* kind,
-                                          int b, MlaSlice* sl, int* per, int* nsp) {
-  int64_t total = 0;
-  for (int i = 0; i < a.batch; ++i) total += mla_slice(a, state + 4 * i, kind[i]).len;
-  int64_t target = (total + a.n_cu - 1) / a.n_cu;
-  if (target < 64) target = 64;
-  target = (target + TK - 1) / TK * TK;
-  *sl = mla_slice(a, state + 4 * b, kind[b]);
-  int64_t p = target;
-  if ((sl->len + p - 1) / p > a.smax) p = ((sl->len + a.smax - 1) / a.smax + TK - 1) / TK * TK;
-  *per = static_cast<int>(p);
-  *nsp = static_cast<int>((sl->len + p - 1) / p);
-}
+// Per-sequence plan, computed once per call by mla_plan_kernel:
+// {slice start, slice length, rows per range, number of ranges}, followed
+// by a work list of (sequence, range) pairs, one per split workgroup.
+struct MlaPlan {
+  int32_t start, len, per, nsp, first, pad0, pad1, pad2;  // first: index of its first work item
+};
+
+constexpr int kMlaCuCap = 1024;  // CU counts above this are clamped
 
 }  // namespace
 
 // Record of one (sequence, range, head): {m (log2 units), l} as two floats,
-// then 512 bf16 of the unnormalised output.
+// then 512 bf16 of the unnormalised output.  The workspace starts with the
+// per-sequence plans (256-byte aligned), then the records.
 constexpr int kMlaRec = 8 + DV * 2;
+
+// Work-list capacity: with ranges of ceil(total / n_cu) rows there are at
+// most n_cu + batch of them.
+__host__ __device__ __forceinline__ int mla_max_items(int batch) { return kMlaCuCap + batch; }
+
+__host__ __device__ __forceinline__ size_t mla_plan_bytes(int batch) {
+  return (static_cast<size_t>(batch) * sizeof(MlaPlan) + sizeof(int32_t) * 2 * mla_max_items(batch) + 255) /
+         256 * 256;
+}
+
+// Cut every slice into ranges of about (total rows / CU count) rows, at least
+// 64, and list the (sequence, range) work items.  One workgroup, one thread
+// per sequence (batch <= 1024).
+__global__ void __launch_bounds__(1024) mla_plan_kernel(MlaArgs a, const int32_t* __restrict__ state,
+                                                        const int32_t* __restrict__ kind,
+                                                        MlaPlan* __restrict__ plan) {
+  __shared__ int64_t part[1024 / 64];
+  const int b = threadIdx.x;
+  MlaSlice sl = {0, 0};
+  if (b < a.batch && kind[b] >= 0) sl = mla_slice(a, state + 4 * b, kind[b]);
+  int64_t v = sl.len;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  if ((b & 63) == 0) part[b >> 6] = v;
+  __syncthreads();
+  int64_t total = 0;
+  for (int w = 0; w < (static_cast<int>(blockDim.x) + 63) / 64; ++w) total += part[w];
+  // ranges of total / (n_cu - batch) rows give at most n_cu ranges, so the
+  // two head groups fill exactly two rounds of workgroups
+  const int64_t slots = a.n_cu - a.batch > a.n_cu / 2 ? a.n_cu - a.batch : a.n_cu / 2;
+  int64_t target = (total + slots - 1) / slots;
+  if (target < 64) target = 64;
+  target = (target + TK - 1) / TK * TK;
+  __shared__ int32_t nsp_s[1024];
+  MlaPlan pl;
+  pl.start = sl.start;
+  pl.len = sl.len;
+  pl.per = static_cast<int32_t>(target);
+  pl.nsp = static_cast<int32_t>((sl.len + target - 1) / target);
+  nsp_s[b] = b < a.batch ? pl.nsp : 0;
+  __syncthreads();
+  // work list: item i -> (sequence, range); unused items get sequence -1
+  int32_t* items = reinterpret_cast<int32_t*>(plan + a.batch);
+  if (b < a.batch) {
+    int first = 0;
+    for (int i = 0; i < b; ++i) first += nsp_s[i];
+    pl.first = first;
+    plan[b] = pl;
+    for (int r = 0; r < pl.nsp; ++r) {
+      items[2 * (first + r)] = b;
+      items[2 * (first + r) + 1] = r;
+    }
+  }
+  int used = 0;
+  for (int i = 0; i < a.batch; ++i) used += nsp_s[i];
+  for (int i = used + b; i < mla_max_items(a.batch); i += blockDim.x) items[2 * i] = -1;
+}
 
 __global__ void __launch_bounds__(512, 1) decode_mla_split_kernel(
     MlaArgs a, const bf16_t* __restrict__ ck, const int32_t* __restrict__ state,
     const bf16_t* __restrict__ q, const int32_t* __restrict__ kind, char* __restrict__ ws) {
-  __shared__ __attribute__((aligned(16))) char lds[NBUF][TILE_LDS];
-  __shared__ __attribute__((aligned(16))) float xs[NW][16][64];  // partial S^T exchange
-  const int sp = blockIdx.x;
-  const int b = blockIdx.y;
-  if (kind[b] < 0) return;
-  MlaSlice sl;
-  int per, nsp;
-  mla_split(a, state, kind, b, &sl, &per, &nsp);
+  __shared__ __attribute__((aligned(16))) char lds[2][TILE_LDS];
+  // partial S^T exchange: lane-major, 16 values + 4 padding per lane
+  __shared__ __attribute__((aligned(16))) float xs[NW][64][20];
+  const int hg = blockIdx.y;  // heads 64 hg .. 64 hg + 63
+  const int32_t* items = reinterpret_cast<const int32_t*>(reinterpret_cast<const MlaPlan*>(ws) + a.batch);
+  const int b = items[2 * blockIdx.x];
+  if (b < 0) return;  // uniform over the block
+  const int sp = items[2 * blockIdx.x + 1];
+  const MlaPlan pl = reinterpret_cast<const MlaPlan*>(ws)[b];
+  const MlaSlice sl = {pl.start, pl.len};
+  const int per = pl.per, nsp = pl.nsp;
   if (sp >= nsp) return;  // uniform over the block
   const int r0 = sp * per;
   const int r1 = r0 + per < sl.len ? r0 + per : sl.len;
@@ -127,81 +192,112 @@ __global__ void __launch_bounds__(512, 1) decode_mla_split_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int hb = wave >> 1;  // head block: heads 32 hb .. 32 hb + 31
-  const int hh = wave & 1;   // key columns 288 hh .., value columns 256 hh ..
+  const int hb = wave >> 2;  // head block: heads 64 hg + 32 hb .. + 31
+  const int qu = wave & 3;   // key columns 144 qu .., value columns 128 qu ..
   const int half = lane >> 5;
   const bf16_t* kseq = ck + (static_cast<int64_t>(b) * a.slots + sl.start + r0) * DQK;
 
-  // Q^T (this wave's key-column half) as the B operand of S^T = K Q^T:
-  // column = head 32 hb + lane % 32, k-slots d = 288 hh + 16 ks + 8 half + j.
-  bf16x8_t qop[18];
+  // Q^T (this wave's key-column quarter) as the B operand of S^T = K Q^T:
+  // column = head (lane % 32 of the block), k-slots d = 144 qu + 16 ks + 8 half + j.
+  bf16x8_t qop[9];
   {
-    const bf16_t* qp =
-        q + (static_cast<int64_t>(b) * HQ + 32 * hb + (lane & 31)) * DQK + 288 * hh + 8 * half;
+    const bf16_t* qp = q + (static_cast<int64_t>(b) * HQ + HWG * hg + 32 * hb + (lane & 31)) * DQK +
+                       144 * qu + 8 * half;
 #pragma unroll
-    for (int ks = 0; ks < 18; ++ks) qop[ks] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * ks);
+    for (int ks = 0; ks < 9; ++ks) qop[ks] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * ks);
   }
 
   // Tile copy: lane chunk s = LOADS_PER_WAVE * 64 * wave + 64 i + lane of the
   // tile maps to row s / 73, chunk s % 73 (chunk 72 is padding and repeats
-  // chunk 71; rows past the tile repeat its last row).
-  auto issue_tile = [&](int t, int buf) {
-    const int rows = (r1 - r0) - t * TK;  // rows left from this tile on (>= 1)
-    const int last = (rows < TK ? rows : TK) - 1;
-    const bf16_t* base = kseq + static_cast<int64_t>(t) * TK * DQK;
+  // chunk 71; rows past the tile repeat its last row).  Offsets are bytes
+  // from the tile's first row.
+  // Tile copy through a buffer resource covering exactly this range's rows:
+  // a lane past the range reads zeros instead of faulting, so the last,
+  // partial tile needs no clamping.  Lane chunk s = LOADS_PER_WAVE * 64 *
+  // wave + 64 i + lane of a tile is row s / 73, 16-byte chunk s % 73 (chunk 72
+  // is row padding in LDS and just reads the next row's first chunk).
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(kseq), static_cast<short>(0), (r1 - r0) * (DQK * 2), 0x00020000);
+  int voff[LOADS_PER_WAVE];
 #pragma unroll
-    for (int i = 0; i < LOADS_PER_WAVE; ++i) {
-      const int s_ = (LOADS_PER_WAVE * wave + i) * 64 + lane;
-      int row = s_ / RCH;
-      int ch = s_ - row * RCH;
-      row = row < last ? row : last;
-      ch = ch < 72 ? ch : 71;
-      char* dst = lds[buf] + (LOADS_PER_WAVE * wave + i) * 1024;
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(base + row * DQK + 8 * ch),
-          (__attribute__((address_space(3))) void*)((__attribute__((address_space(3))) char*)dst), 16, 0,
-          0);
-    }
+  for (int i = 0; i < LOADS_PER_WAVE; ++i) {
+    const int s_ = (LOADS_PER_WAVE * wave + i) * 64 + lane;
+    const int row = s_ / RCH;
+    voff[i] = row * (DQK * 2) + 16 * (s_ - row * RCH);
+  }
+  u32x4_t kreg[LOADS_PER_WAVE];
+  auto prefetch = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < LOADS_PER_WAVE; ++i)
+      kreg[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                rsrc, voff[i], t * TK * DQK * 2, 0));
+  };
+  auto store = [&](char* buf) {
+#pragma unroll
+    for (int i = 0; i < LOADS_PER_WAVE; ++i)
+      *reinterpret_cast<u32x4_t*>(buf + (LOADS_PER_WAVE * wave + i) * 1024 + 16 * lane) = kreg[i];
   };
 
-  f32x16_t oacc[8];
+  f32x16_t oacc[4];
 #pragma unroll
-  for (int db = 0; db < 8; ++db)
+  for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
   float m_ref = kNegInf, l_run = 0.f;
   const uint32_t one2 = 0x3f803f80u;
 
   // per-lane LDS offsets
-  const int krow_off = (lane & 31) * RB + 16 * half + 576 * hh;
+  const int krow_off = (lane & 31) * RB + 16 * half + 288 * qu;
   const int G = lane >> 4, l16 = lane & 15, rr = l16 >> 2, c4 = l16 & 3;
-  const int vrow_off = (4 * (G >> 1) + rr) * RB + 2 * (16 * (G & 1) + 4 * c4) + 512 * hh;
+  const int vrow_off = (4 * (G >> 1) + rr) * RB + 2 * (16 * (G & 1) + 4 * c4) + 256 * qu;
 
-  for (int t = 0; t < NBUF - 1 && t < ntile; ++t) issue_tile(t, t);
-  for (int t = 0; t < ntile; ++t) {
-    // tile t must be complete: later tiles' loads may stay in flight
-    if (t + 1 < ntile)
-      __builtin_amdgcn_s_waitcnt(0x0f70 | (LOADS_PER_WAVE & 15) | ((LOADS_PER_WAVE >> 4) << 14));
-    else
-      __builtin_amdgcn_s_waitcnt(0x0f70);
-    __syncthreads();
-    if (t + NBUF - 1 < ntile) issue_tile(t + NBUF - 1, (t + NBUF - 1) % NBUF);
-    const char* kl = lds[t % NBUF];
+  if (ntile > 0) {
+    prefetch(0);
+    store(lds[0]);
+  }
+  __syncthreads();
+  auto tile_step = [&](auto cur_c, int t) {
+    constexpr int cur = decltype(cur_c)::value;
+    if (t + 1 < ntile) prefetch(t + 1);  // in flight during this tile
+    const char* kl = lds[cur];
 
-    // ---- this wave's half of S^T = K Q^T ----
-    f32x16_t s;
+    // ---- this wave's quarter of S^T = K Q^T ----
+    // three independent accumulation chains keep the MFMA pipe busy
+    f32x16_t s, s1, s2;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+    for (int r = 0; r < 16; ++r) s[r] = s1[r] = s2[r] = 0.f;
+    {
+      bf16x8_t kop[9];  // all operand reads issued before the MFMAs
 #pragma unroll
-    for (int ks = 0; ks < 18; ++ks) {
-      const bf16x8_t kop = *reinterpret_cast<const bf16x8_t*>(kl + krow_off + 32 * ks);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[ks], s, 0, 0, 0);
+      for (int ks = 0; ks < 9; ++ks) kop[ks] = *reinterpret_cast<const bf16x8_t*>(kl + krow_off + 32 * ks);
+#pragma unroll
+      for (int ks = 0; ks < 9; ks += 3) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qop[ks], s, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks + 1], qop[ks + 1], s1, 0, 0, 0);
+        s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks + 2], qop[ks + 2], s2, 0, 0, 0);
+      }
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) xs[wave][r][lane] = s[r];
-    __syncthreads();
+    for (int r = 0; r < 16; ++r) s[r] += s1[r] + s2[r];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] += xs[wave ^ 1][r][lane];
+    for (int r = 0; r < 16; r += 4)
+      *reinterpret_cast<f32x4_t*>(&xs[wave][lane][r]) = (f32x4_t){s[r], s[r + 1], s[r + 2], s[r + 3]};
+    // exchange written (lgkmcnt(0)); the prefetch stays in flight, so a bare
+    // s_barrier rather than __syncthreads
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    wg_barrier();
+    {
+      f32x4_t part[3][4];
+#pragma unroll
+      for (int o = 1; o < 4; ++o)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          part[o - 1][r] = *reinterpret_cast<const f32x4_t*>(&xs[(wave & ~3) | ((qu + o) & 3)][lane][4 * r]);
+#pragma unroll
+      for (int o = 0; o < 3; ++o)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] += part[o][r >> 2][r & 3];
+    }
     // ---- softmax: lane = head, registers = keys 8 (r/4) + 4 half + r%4 ----
     const int valid = (r1 - r0) - t * TK;
     if (valid < TK) {
@@ -219,7 +315,7 @@ __global__ void __launch_bounds__(512, 1) decode_mla_split_kernel(
       m_ref = m_new;
       l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < 8; ++db)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
     }
@@ -232,12 +328,12 @@ __global__ void __launch_bounds__(512, 1) decode_mla_split_kernel(
       l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w),
                                               __builtin_bit_cast(bf16x2_t, one2), l_run, false);
     }
-    // ---- this wave's half of O^T += V^T P^T (V = first 512 key columns) ----
+    // ---- this wave's quarter of O^T += V^T P^T (V = first 512 key columns) ----
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, pw[ks]);
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
+      for (int db = 0; db < 4; ++db) {
         const int off = vrow_off + 16 * ks * RB + 64 * db;
         const bf16x4_t lo = lds_read_tr(kl, off);
         const bf16x4_t hi = lds_read_tr(kl, off + 8 * RB);
@@ -245,19 +341,25 @@ __global__ void __launch_bounds__(512, 1) decode_mla_split_kernel(
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop, oacc[db], 0, 0, 0);
       }
     }
+    if (t + 1 < ntile) store(lds[cur ^ 1]);
+    __syncthreads();
+  };
+  for (int t = 0; t < ntile; t += 2) {
+    tile_step(std::integral_constant<int, 0>(), t);
+    if (t + 1 < ntile) tile_step(std::integral_constant<int, 1>(), t + 1);
   }
 
-  // ---- write this range's partial (both halves hold the same m and l) ----
+  // ---- write this range's partial (the four quarters hold the same m and l) ----
   const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const int head = 32 * hb + (lane & 31);
-  char* rec = ws + ((static_cast<int64_t>(b) * a.smax + sp) * HQ + head) * kMlaRec;
-  if (half == 0 && hh == 0) {
+  const int head = HWG * hg + 32 * hb + (lane & 31);
+  char* rec = ws + mla_plan_bytes(a.batch) + ((static_cast<int64_t>(blockIdx.x)) * HQ + head) * kMlaRec;
+  if (half == 0 && qu == 0) {
     reinterpret_cast<float*>(rec)[0] = m_ref;
     reinterpret_cast<float*>(rec)[1] = l_tot;
   }
-  bf16_t* ro = reinterpret_cast<bf16_t*>(rec + 8) + 256 * hh;
+  bf16_t* ro = reinterpret_cast<bf16_t*>(rec + 8) + 128 * qu;
 #pragma unroll
-  for (int db = 0; db < 8; ++db)
+  for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
       const int d = 32 * db + 8 * qq + 4 * half;
@@ -268,7 +370,7 @@ __global__ void __launch_bounds__(512, 1) decode_mla_split_kernel(
     }
 }
 
-__global__ void __launch_bounds__(256) decode_mla_merge_kernel(MlaArgs a, const int32_t* __restrict__ state,
+__global__ void __launch_bounds__(256) decode_mla_merge_kernel(MlaArgs a,
                                                                const int32_t* __restrict__ kind,
                                                                const char* __restrict__ ws,
                                                                bf16_t* __restrict__ out,
@@ -276,25 +378,43 @@ __global__ void __launch_bounds__(256) decode_mla_merge_kernel(MlaArgs a, const 
   const int head = blockIdx.x;
   const int b = blockIdx.y;
   if (kind[b] < 0) return;
-  MlaSlice sl;
-  int per, nsp;
-  mla_split(a, state, kind, b, &sl, &per, &nsp);
-  const char* rec0 = ws + (static_cast<int64_t>(b) * a.smax * HQ + head) * kMlaRec;
+  const MlaPlan pl = reinterpret_cast<const MlaPlan*>(ws)[b];
+  const int nsp = pl.nsp;
+  const char* rec0 = ws + mla_plan_bytes(a.batch) + (static_cast<int64_t>(pl.first) * HQ + head) * kMlaRec;
   const int64_t stride = static_cast<int64_t>(HQ) * kMlaRec;
-  float mx = kNegInf;
-  for (int s = 0; s < nsp; ++s) mx = fmaxf(mx, reinterpret_cast<const float*>(rec0 + s * stride)[0]);
-  const float mu = mx == kNegInf ? 0.f : mx;
-  float l = 0.f;
-  for (int s = 0; s < nsp; ++s) {
-    const float* h = reinterpret_cast<const float*>(rec0 + s * stride);
-    l += fast_exp2(h[0] - mu) * h[1];
+  // weights of every range, computed once per block into LDS
+  __shared__ float wgt[256];
+  __shared__ float red[2];
+  if (threadIdx.x < 64) {
+    float mloc = kNegInf;
+    for (int s = threadIdx.x; s < nsp; s += 64)
+      mloc = fmaxf(mloc, reinterpret_cast<const float*>(rec0 + s * stride)[0]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o));
+    const float mu = mloc == kNegInf ? 0.f : mloc;
+    float lloc = 0.f;
+    for (int s = threadIdx.x; s < nsp; s += 64) {
+      const float* h = reinterpret_cast<const float*>(rec0 + s * stride);
+      const float w = fast_exp2(h[0] - mu);
+      if (s < 256) wgt[s] = w;
+      lloc += w * h[1];
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) lloc += __shfl_xor(lloc, o);
+    if (threadIdx.x == 0) {
+      red[0] = mloc;
+      red[1] = lloc;
+    }
   }
+  __syncthreads();
+  const float mx = red[0], l = red[1];
+  const float mu = mx == kNegInf ? 0.f : mx;
   const float inv = l > 0.f ? 1.f / l : 0.f;
   for (int d = 2 * threadIdx.x; d < DV; d += 2 * blockDim.x) {
     float o0 = 0.f, o1 = 0.f;
     for (int s = 0; s < nsp; ++s) {
       const char* r = rec0 + s * stride;
-      const float w = fast_exp2(reinterpret_cast<const float*>(r)[0] - mu);
+      const float w = s < 256 ? wgt[s] : fast_exp2(reinterpret_cast<const float*>(r)[0] - mu);
       const uint32_t v = *reinterpret_cast<const uint32_t*>(r + 8 + 2 * d);
       o0 += w * __uint_as_float(v << 16);
       o1 += w * __uint_as_float(v & 0xffff0000u);
@@ -308,13 +428,13 @@ __global__ void __launch_bounds__(256) decode_mla_merge_kernel(MlaArgs a, const 
 
 bool decode_mla_supported(const DecodeArgs& a, int32_t dtype) {
   return dtype == KSA_DTYPE_BF16 && a.v_is_k_prefix && a.dqk == DQK && a.dv == DV && a.hq == HQ &&
-         a.hkv == 1 && a.slots < (int64_t(1) << 31) / DQK;
+         a.hkv == 1 && a.batch <= 1024 && a.slots < (int64_t(1) << 31) / DQK;
 }
 
-constexpr int kMlaMaxSplits = 64;
 
 size_t decode_mla_workspace_bytes(const DecodeArgs& a) {
-  return static_cast<size_t>(a.batch) * kMlaMaxSplits * HQ * kMlaRec;
+  const size_t plan = mla_plan_bytes(a.batch);
+  return plan + static_cast<size_t>(kMlaCuCap + a.batch) * HQ * kMlaRec;
 }
 
 hipError_t launch_decode_mla(const DecodeArgs& d, const void* ck, const int32_t* state, const void* q,
@@ -325,18 +445,22 @@ hipError_t launch_decode_mla(const DecodeArgs& d, const void* ck, const int32_t*
   a.C = d.C;
   a.max_summaries = d.max_summaries;
   a.slots = d.slots;
-  a.smax = kMlaMaxSplits;
+  a.smax = 0;
   a.sl = d.scale * kLog2e;
   int dev = 0, ncu = 256;
   if (hipGetDevice(&dev) == hipSuccess)
     hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-  a.n_cu = ncu > 0 ? ncu : 256;
-  hipLaunchKernelGGL(decode_mla_split_kernel, dim3(kMlaMaxSplits, d.batch), dim3(512), 0, s, a,
+  a.n_cu = ncu > 0 ? (ncu < kMlaCuCap ? ncu : kMlaCuCap) : 256;
+  hipLaunchKernelGGL(mla_plan_kernel, dim3(1), dim3(((d.batch + 63) / 64) * 64), 0, s, a, state, kind,
+                     static_cast<MlaPlan*>(ws));
+  hipError_t e0 = hipGetLastError();
+  if (e0 != hipSuccess) return e0;
+  hipLaunchKernelGGL(decode_mla_split_kernel, dim3(a.n_cu + d.batch, HQ / HWG), dim3(512), 0, s, a,
                      static_cast<const bf16_t*>(ck), state, static_cast<const bf16_t*>(q), kind,
                      static_cast<char*>(ws));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_mla_merge_kernel, dim3(HQ, d.batch), dim3(256), 0, s, a, state, kind,
+  hipLaunchKernelGGL(decode_mla_merge_kernel, dim3(HQ, d.batch), dim3(256), 0, s, a, kind,
                      static_cast<const char*>(ws), static_cast<bf16_t*>(out), lse);
   return hipGetLastError();
 }
