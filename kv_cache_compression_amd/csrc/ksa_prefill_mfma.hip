@@ -320,13 +320,16 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_d128_kernel(
     }
     if (wave_active && !empty) {
       // ---- S^T = K Q^T: two 32-key blocks ----
+      // the two 32-key blocks are independent MFMA chains; interleave them
       f32x16_t sacc[2];
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
+      for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[kb2][r] = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
+      for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
           const bf16x8_t kop = *reinterpret_cast<const bf16x8_t*>(kl + koff[ks] + 32 * ROW_BYTES * kb2);
           sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[ks], sacc[kb2], 0, 0, 0);
         }
