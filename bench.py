@@ -73,11 +73,15 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-long", action="store_true", help="skip the 131072-token prefill lines")
     ap.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0 = auto)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 256 MiB device copy three times (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; multi-GPU runs are not part of it",
+        print(json.dumps({"error": "this benchmark measures one GPU only; runs on several GPUs are not supported",
                           "n_gpus": args.gpus}))
         return 2
+    if args.copy_probe:
+        return copy_probe()
 
     import torch
 
@@ -244,10 +248,58 @@ def main() -> int:
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": None},
     }
+    traffic = prefill_traffic()
+    if traffic is not None:
+        res["roofline"]["traffic"] = traffic["total_bytes"]
+        res["roofline"]["traffic_detail"] = traffic
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
     print(json.dumps(res), flush=True)
     return 0
+
+
+COPY_PROBE_BYTES = 256 << 20
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "prefill_mfma_d128_32k_pmc.txt")
+PREFILL_SOURCE = os.path.join(ROOT, "kv_cache_compression_amd", "csrc", "ksa_prefill_mfma.hip")
+
+
+def copy_probe() -> int:
+    """A plain device-to-device copy of known size, used to scale the
+    FETCH_SIZE / WRITE_SIZE hardware counters to bytes."""
+    import torch
+
+    a = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": COPY_PROBE_BYTES, "copies": 3}), flush=True)
+    return 0
+
+
+def prefill_traffic():
+    """HBM bytes per prefill launch from the committed counter summary, or
+    None when the summary is missing or the kernel source has changed since
+    the counters were taken."""
+    import hashlib
+
+    try:
+        kv = {}
+        with open(PMC_SUMMARY) as f:
+            for line in f:
+                if "=" in line and not line.lstrip().startswith("#"):
+                    key, val = line.split("=", 1)
+                    kv[key.strip()] = val.strip()
+        with open(PREFILL_SOURCE, "rb") as f:
+            digest = hashlib.sha256(f.read()).hexdigest()
+        if kv.get("kernel_source_sha256") != digest:
+            return None
+        fetch = float(kv["fetch_kib_per_dispatch"]) * float(kv["fetch_scale"]) * 1024
+        write = float(kv["write_kib_per_dispatch"]) * float(kv["write_scale"]) * 1024
+        return {"read_bytes": int(fetch), "write_bytes": int(write), "total_bytes": int(fetch + write),
+                "algorithmic_bytes": int(kv["algorithmic_bytes"]), "source": os.path.relpath(PMC_SUMMARY, ROOT)}
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def prefill_long(ksa, ksa_synth, torch, dev, stream, reps: int = 5) -> list:
