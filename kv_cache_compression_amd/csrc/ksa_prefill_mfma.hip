@@ -11,8 +11,8 @@
 // tiles; only tiles on a run's edge need an element mask, computed from
 // integer compares on chunk indices.  A summary query s_j reads only its own
 // chunk's k text tokens and itself (Sec. 2.2.1), i.e. the k+1 consecutive
-// augmented rows j(k+1) .. j(k+1)+k; those rows are handled by extra
-// workgroups at the end of the same launch.
+// augmented rows j(k+1) .. j(k+1)+k; those rows are handled by the first
+// workgroups of the same launch (one wave per summary and kv head).
 //
 // Text workgroups (4 wavefronts, 256 threads):
 //   - a workgroup owns one kv head and HPW of its query heads over PT
@@ -24,10 +24,17 @@
 //   - O^T += V^T P^T on the same MFMA: P goes from the score registers into
 //     the B operand; V^T comes from the row-major V tile through
 //     ds_read_b64_tr_b16 (4x16 bf16 transposes within each 16 lanes);
+//   - software pipeline over tiles: while the MFMAs of S for tile t+1 run,
+//     the VALU turns the scores of tile t into P; while the MFMAs of P V for
+//     tile t run, the VALU finishes P, masks tile t+1 and takes its maximum;
 //   - the running maximum is only moved (and O rescaled) when a tile's
 //     maximum exceeds it by more than 2^8, which keeps every exponent <= 8;
-//   - K/V tiles are double-buffered in LDS and prefetched one tile ahead
-//     into registers: one barrier per tile;
+//     that decision is taken one tile ahead, so no branch splits the
+//     MFMA/VALU interleave;
+//   - K/V tiles go straight from global memory into double-buffered LDS
+//     (buffer_load ... lds, swizzle applied on the global side), one tile
+//     ahead, through buffer resources with 32-bit row offsets: one barrier
+//     per tile, no staging registers;
 //   - workgroups run longest-first (later queries see more summaries) and,
 //     when the head count allows, all workgroups of one (sequence, kv head)
 //     sit on one XCD so that its K/V stay in that XCD's L2.
@@ -54,7 +61,7 @@ typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 
 struct MfmaArgs {
   int32_t batch, n, L, k, C, hq, hkv, g, M;
-  int32_t n_tiles, n_hg, xcd_map, n_text_blocks;
+  int32_t n_tiles, n_hg, xcd_map, n_text_blocks, n_sum_blocks;
   uint32_t divk_m, divk_l;  // floor(t / k) = (umulhi(t, m) + t) >> l for t < 2^31
   float sl;                 // softmax scale * log2(e)
 };
@@ -64,7 +71,6 @@ __device__ __forceinline__ int32_t div_k(const MfmaArgs& a, int32_t t) {
                               a.divk_l);
 }
 __device__ __forceinline__ int32_t trow(const MfmaArgs& a, int32_t t) { return t + div_k(a, t); }
-__device__ __forceinline__ int32_t srow(const MfmaArgs& a, int32_t j) { return j * (a.k + 1) + a.k; }
 
 // 16-byte chunk c (0..15) of LDS row `row` is stored at chunk c ^ swz(row):
 // 8 consecutive rows hit 8 different even chunks and the next 8 the odd
@@ -87,72 +93,82 @@ __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Summary query rows: one wave per (sequence, kv head, summary j); it
-// attends every query head of the group to the k+1 rows j(k+1) .. j(k+1)+k.
-// Lanes: 16 per key row (8 bf16 of d each), 4 rows per pass.
+// Summary query rows: one wave per (sequence, kv head, summary j) attends
+// the group's query heads to the k + 1 rows j(k+1) .. j(k+1)+k.  Lane
+// (hh, c) = (lane / 16, lane % 16) holds dims 8c .. 8c+7 of head hh of a
+// group of four; the key/value rows of a pass are all loaded before any is
+// used, so a pass costs one memory round trip.
+constexpr int SUM_R = 16;  // key rows per pass
+
+// Takes the word by value: __builtin_bit_cast applied directly to a vector
+// element (v.y) reads element 0 with this compiler.
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2_t, w); }
 __device__ void summary_rows_wave(const MfmaArgs& a, int64_t item, const bf16_t* __restrict__ q,
                                   const bf16_t* __restrict__ kx, const bf16_t* __restrict__ vx,
                                   bf16_t* __restrict__ out, float* __restrict__ lse) {
   const int lane = threadIdx.x & 63;
-  const int c = lane & 15;    // d chunk: d = 8 c .. 8 c + 7
-  const int grp = lane >> 4;  // row slot within a pass
+  const int c = lane & 15;
+  const int hh = lane >> 4;
   const int j = static_cast<int>(item % a.M);
   const int kvh = static_cast<int>((item / a.M) % a.hkv);
   const int b = static_cast<int>(item / (static_cast<int64_t>(a.M) * a.hkv));
   const int r0 = j * (a.k + 1);
   const int nrows = a.k + 1;
+  const int srow_a = r0 + a.k;  // the summary's own augmented row
   const int64_t kvs = static_cast<int64_t>(a.hkv) * D;
   const bf16_t* kb = kx + static_cast<int64_t>(b) * a.L * kvs + kvh * D + 8 * c;
   const bf16_t* vb = vx + static_cast<int64_t>(b) * a.L * kvs + kvh * D + 8 * c;
-  const int srow_a = r0 + a.k;  // the summary's own augmented row
-  for (int hh = 0; hh < a.g; ++hh) {
-    const int h = kvh * a.g + hh;
+  for (int hg = 0; hg < a.g; hg += 4) {
+    const int hloc = hg + hh;
+    const bool hval = hloc < a.g;
+    const int h = kvh * a.g + (hval ? hloc : 0);
     const u32x4_t qw = *reinterpret_cast<const u32x4_t*>(
         q + (static_cast<int64_t>(b) * a.L + srow_a) * a.hq * D + static_cast<int64_t>(h) * D + 8 * c);
-    const float qf[8] = {bf_lo(qw.x), bf_hi(qw.x), bf_lo(qw.y), bf_hi(qw.y),
-                         bf_lo(qw.z), bf_hi(qw.z), bf_lo(qw.w), bf_hi(qw.w)};
     float m = kNegInf, l = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < nrows; s0 += 4) {
-      const int slot = s0 + grp;
-      const bool ok = slot < nrows;
-      const int row = r0 + (ok ? slot : 0);
-      const u32x4_t kw = *reinterpret_cast<const u32x4_t*>(kb + row * kvs);
-      float part = qf[0] * bf_lo(kw.x) + qf[1] * bf_hi(kw.x) + qf[2] * bf_lo(kw.y) +
-                   qf[3] * bf_hi(kw.y) + qf[4] * bf_lo(kw.z) + qf[5] * bf_hi(kw.z) +
-                   qf[6] * bf_lo(kw.w) + qf[7] * bf_hi(kw.w);
-      part += __shfl_xor(part, 8);
-      part += __shfl_xor(part, 4);
-      part += __shfl_xor(part, 2);
-      part += __shfl_xor(part, 1);
-      const float s = ok ? part * a.sl : kNegInf;
-      const float mn = fmaxf(m, s);
-      const float mu = mn == kNegInf ? 0.f : mn;
-      const float al = fast_exp2(m - mu);
-      const float p = fast_exp2(s - mu);
-      const u32x4_t vw = *reinterpret_cast<const u32x4_t*>(vb + row * kvs);
-      const float vf[8] = {bf_lo(vw.x), bf_hi(vw.x), bf_lo(vw.y), bf_hi(vw.y),
-                           bf_lo(vw.z), bf_hi(vw.z), bf_lo(vw.w), bf_hi(vw.w)};
-      l = l * al + p;
+    for (int s0 = 0; s0 < nrows; s0 += SUM_R) {
+      u32x4_t kw[SUM_R], vw[SUM_R];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = o[e] * al + p * vf[e];
-      m = mn;
-    }
-    // merge the four row slots (lane groups 16 apart); a group that saw no
-    // row (k + 1 < 4) carries m = -inf and contributes nothing
-    float mx = fmaxf(m, __shfl_xor(m, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float w = m == kNegInf ? 0.f : fast_exp2(m - mx);
-    l *= w;
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+      for (int r = 0; r < SUM_R; ++r) {
+        const int row = r0 + min(s0 + r, nrows - 1);
+        kw[r] = *reinterpret_cast<const u32x4_t*>(kb + row * kvs);
+        vw[r] = *reinterpret_cast<const u32x4_t*>(vb + row * kvs);
+      }
+      float sc[SUM_R];
+      float mx = m;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float x = o[e] * w;
-      x += __shfl_xor(x, 16);
-      x += __shfl_xor(x, 32);
-      o[e] = x;
+      for (int r = 0; r < SUM_R; ++r) {
+        float part = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qw.x),
+                                                     as_bf16x2(kw[r].x), 0.f, false);
+        part = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qw.y),
+                                               as_bf16x2(kw[r].y), part, false);
+        part = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qw.z),
+                                               as_bf16x2(kw[r].z), part, false);
+        part = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qw.w),
+                                               as_bf16x2(kw[r].w), part, false);
+        part += __shfl_xor(part, 8);
+        part += __shfl_xor(part, 4);
+        part += __shfl_xor(part, 2);
+        part += __shfl_xor(part, 1);
+        sc[r] = s0 + r < nrows ? part * a.sl : kNegInf;
+        mx = fmaxf(mx, sc[r]);
+      }
+      const float al = m == kNegInf ? 0.f : fast_exp2(m - mx);
+      l *= al;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] *= al;
+#pragma unroll
+      for (int r = 0; r < SUM_R; ++r) {
+        const float p = fast_exp2(sc[r] - mx);
+        l += p;
+        const u32x4_t w = vw[r];
+        o[0] += p * bf_lo(w.x); o[1] += p * bf_hi(w.x);
+        o[2] += p * bf_lo(w.y); o[3] += p * bf_hi(w.y);
+        o[4] += p * bf_lo(w.z); o[5] += p * bf_hi(w.z);
+        o[6] += p * bf_lo(w.w); o[7] += p * bf_hi(w.w);
+      }
+      m = mx;
     }
-    if (grp == 0) {
+    if (hval) {
       const float inv = 1.f / l;
       u32x4_t ow;
       ow.x = pk_bf16(o[0] * inv, o[1] * inv);
@@ -162,7 +178,7 @@ __device__ void summary_rows_wave(const MfmaArgs& a, int64_t item, const bf16_t*
       *reinterpret_cast<u32x4_t*>(out + (static_cast<int64_t>(b) * a.L + srow_a) * a.hq * D +
                                   static_cast<int64_t>(h) * D + 8 * c) = ow;
       if (lse && c == 0)
-        lse[(static_cast<int64_t>(b) * a.hq + h) * a.L + srow_a] = (mx + log2f(l)) * kLn2;
+        lse[(static_cast<int64_t>(b) * a.hq + h) * a.L + srow_a] = (m + log2f(l)) * kLn2;
     }
   }
 }
@@ -174,19 +190,18 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_d128_kernel(
     MfmaArgs a, const bf16_t* __restrict__ q, const bf16_t* __restrict__ kx,
     const bf16_t* __restrict__ vx, bf16_t* __restrict__ out, float* __restrict__ lse) {
   constexpr int PT = 32 * (4 / HPW);  // text positions per workgroup
-  __shared__ __attribute__((aligned(16))) char lds[2][2][TILE_BYTES];  // [buffer][K, V]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  if (static_cast<int>(blockIdx.x) >= a.n_text_blocks) {
-    const int64_t item = static_cast<int64_t>(blockIdx.x - a.n_text_blocks) * 4 + wave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (static_cast<int>(blockIdx.x) < a.n_sum_blocks) {
+    const int64_t item = static_cast<int64_t>(blockIdx.x) * 4 + wave;
     if (item < static_cast<int64_t>(a.batch) * a.hkv * a.M) summary_rows_wave(a, item, q, kx, vx, out, lse);
     return;
   }
 
   const int n_slots = a.batch * a.hkv * a.n_hg;
-  const int bid = blockIdx.x;
+  const int bid = blockIdx.x - a.n_sum_blocks;
   int hslot, t_rev;
   if (a.xcd_map) {  // blocks are dispatched round-robin over the 8 XCDs
     const int x = bid & 7, s = bid >> 3;
@@ -222,7 +237,6 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_d128_kernel(
   const int tlo = q_valid ? (ci - a.C > 0 ? (ci - a.C) * a.k : 0) : 0x7fffffff;
   const int thi = qi;
   const int cw0 = div_k(a, wave_active ? iw0 : 0), cw1 = div_k(a, wave_active ? iw1 : 0);
-  const int tlo_w0 = cw0 - a.C > 0 ? (cw0 - a.C) * a.k : 0;
   const int tlo_w1 = cw1 - a.C > 0 ? (cw1 - a.C) * a.k : 0;
 
   // Q^T as the B operand: column = query (lane % 32), k-slots
@@ -238,57 +252,72 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_d128_kernel(
       qop[ks] = q_valid ? *reinterpret_cast<const bf16x8_t*>(qp + 16 * ks) : bf16x8_t{};
   }
 
-  // Global -> register prefetch of one K and one V tile: thread owns 16-byte
-  // chunk (tid % 16) of rows tid/16 + 16 u.
+  // Global -> register prefetch: thread owns 16-byte chunk (tid % 16) of
+  // rows tid/16 + 16 u of a tile.  Tile indices are clamped to the last
+  // tile, so loads are always in range and the loop body has no branches.
   const int ld_chunk = tid & 15;
   const int ld_row = tid >> 4;
   const int kvs = a.hkv * D;  // elements per augmented row
-  const bf16_t* kb = kx + static_cast<int64_t>(b) * a.L * kvs + kvh * D + 8 * ld_chunk;
-  const bf16_t* vb = vx + static_cast<int64_t>(b) * a.L * kvs + kvh * D + 8 * ld_chunk;
-  u32x4_t kreg[4], vreg[4];
-#define KSA_PREFETCH(tt)                                                          \
-  do {                                                                            \
-    _Pragma("unroll") for (int u = 0; u < 4; ++u) {                               \
-      const int r_ = ld_row + 16 * u;                                             \
-      int ar_;                                                                    \
-      if ((tt) < ns) {                                                            \
-        const int j_ = (tt) * BN + r_;                                            \
-        ar_ = srow(a, j_ < sn ? j_ : sn - 1);                                     \
-      } else {                                                                    \
-        const int t_ = t0 + ((tt) - ns) * BN + r_;                                \
-        ar_ = trow(a, t_ < p_last ? t_ : p_last);                                 \
-      }                                                                           \
-      kreg[u] = *reinterpret_cast<const u32x4_t*>(kb + ar_ * kvs);                \
-      vreg[u] = *reinterpret_cast<const u32x4_t*>(vb + ar_ * kvs);                \
-    }                                                                             \
-  } while (0)
-#define KSA_STORE(buf)                                                            \
-  do {                                                                            \
-    _Pragma("unroll") for (int u = 0; u < 4; ++u) {                               \
-      const int off_ = lds_off(ld_row + 16 * u, ld_chunk);                        \
-      *reinterpret_cast<u32x4_t*>(&lds[buf][0][off_]) = kreg[u];                  \
-      *reinterpret_cast<u32x4_t*>(&lds[buf][1][off_]) = vreg[u];                  \
-    }                                                                             \
-  } while (0)
+  const int RB = kvs * 2;     // bytes per augmented row
+  const int64_t kv_base = static_cast<int64_t>(b) * a.L * kvs + kvh * D;
+  const int kv_bytes = (a.L * kvs - kvh * D) * 2;
+  const __amdgpu_buffer_rsrc_t rsrc_k = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(kx + kv_base), static_cast<short>(0), kv_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsrc_v = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(vx + kv_base), static_cast<short>(0), kv_bytes, 0x00020000);
+  // direct-to-LDS loads place lane chunks linearly (row tid/16 + 16 u,
+  // physical chunk tid % 16); the thread loads the logical chunk that the
+  // swizzle maps there
+  const int chunk16 = 16 * (ld_chunk ^ (((ld_row & 7) << 1) | ((ld_row >> 3) & 1)));
+  const int sum_step = (a.k + 1) * RB;  // bytes between consecutive summary rows
+  const int s_c0 = ld_row * sum_step + a.k * RB + chunk16;
+  const int s_lim = (sn > 0 ? (sn - 1) * sum_step + a.k * RB : 0) + chunk16;
+  __shared__ __attribute__((aligned(16))) char lds_k0[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char lds_k1[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char lds_v0[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char lds_v1[TILE_BYTES];
+  char* const lds_k[2] = {lds_k0, lds_k1};
+  char* const lds_v[2] = {lds_v0, lds_v1};
+  // byte offsets of this thread's 4 rows of tile tt
+  auto tile_offsets = [&](int tt, int* vo) {
+    if (tt < ns) {
+      const int sb = s_c0 + tt * BN * sum_step;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) vo[u] = min(sb + 16 * u * sum_step, s_lim);
+    } else {
+      const int x0 = t0 + (tt - ns) * BN + ld_row;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int x = min(x0 + 16 * u, p_last);
+        vo[u] = static_cast<int>(__umul24(static_cast<uint32_t>(trow(a, x)), RB)) + chunk16;
+      }
+    }
+  };
+  auto load_tile = [&](const __amdgpu_buffer_rsrc_t& rs, char* buf, int tt) {
+    int vo[4];
+    tile_offsets(tt, vo);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(buf + (64 * wave + 256 * u) * 16), 16, vo[u], 0, 0, 0);
+  };
 
   f32x16_t oacc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  float m_ref = kNegInf;  // reference maximum (log2 units), shared by lanes i and i^32
   float l_run = 0.f;      // this lane's half of the row sum
 
-  // Per-lane LDS byte offsets, fixed for the whole loop (tile rows and
-  // buffers only add constants).  K operand: row lane % 32 (+32), chunk
-  // 2 ks + half.  Transposing V reads: in 16-lane group G, lane (4 rr + c4)
-  // points at key row 16 ks + 8 rd + 4 (G / 2) + rr and d = 32 db + 16 (G % 2)
-  // + 4 c4, and receives V[4 keys][d = 32 db + lane % 32].
-  int koff[8], voff[2][4];
+  // Per-lane LDS byte offsets, fixed for the whole loop.  K operand: row
+  // lane % 32 (+32), chunk 2 ks + half.  Transposing V reads: in 16-lane
+  // group G, lane (4 rr + c4) points at key row 16 ks + 8 rd + 4 (G / 2) + rr
+  // and d = 32 db + 16 (G % 2) + 4 c4, and receives V[4 keys][d = 32 db + lane % 32].
+  // chunk 2 ks + half of a row sits at lds_off(row, half) ^ (ks << 5)
+  int koff0, voff[2][4];
   {
     const int G = lane >> 4, l16 = lane & 15, rr = l16 >> 2, c4 = l16 & 3;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) koff[ks] = lds_off(lane & 31, 2 * ks + half);
+    koff0 = lds_off(lane & 31, half);
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       const int d = 32 * db + 16 * (G & 1) + 4 * c4;
@@ -299,116 +328,140 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_d128_kernel(
   }
   const uint32_t one2 = 0x3f803f80u;  // two bf16 ones
 
-  // One tile: `cur` is a compile-time buffer index so LDS addresses fold
-  // into instruction offsets.
-  auto tile_step = [&](auto cur_c, int tt) {
-    constexpr int cur = decltype(cur_c)::value;
-    if (tt + 1 < n_total) KSA_PREFETCH(tt + 1);
-    const char* kl = lds[cur][0];
-    const char* vl = lds[cur][1];
+  // S^T = K Q^T for one tile: two independent 32-key MFMA chains.
+  auto s_tile = [&](const char* kl, f32x16_t* sacc) {
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[kb2][r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        const bf16x8_t kop = *reinterpret_cast<const bf16x8_t*>(kl + (koff0 ^ (ks << 5)) + 32 * ROW_BYTES * kb2);
+        sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[ks], sacc[kb2], 0, 0, 0);
+      }
+  };
 
-    // Does this tile hold anything for this wave, and does it need a mask?
+  // Mask of tile tt (edge tiles only): visible iff lo <= key <= hi, with
+  // key of (kb2, r) = key0 + 32 kb2 + 8 (r / 4) + 4 half + r % 4.
+  auto mask_tile = [&](int tt, f32x16_t* sacc) {
     const bool is_sum = tt < ns;
     const int key0 = is_sum ? tt * BN : t0 + (tt - ns) * BN;
-    bool empty, full;
-    if (is_sum) {
-      empty = key0 > cw1 - a.C - 1;
+    bool full;
+    if (is_sum)
       full = key0 + BN - 1 <= cw0 - a.C - 1;
-    } else {
-      empty = key0 > iw1 || key0 + BN - 1 < tlo_w0;
+    else
       full = key0 >= tlo_w1 && key0 + BN - 1 <= iw0;
+    if (!full) {
+      const int lo = is_sum ? -1 : tlo;
+      const int hi = is_sum ? smax : thi;
+      const int kbase = key0 + 4 * half;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kbase + 32 * kb2 + 8 * (r >> 2) + (r & 3);
+          sacc[kb2][r] = (key >= lo && key <= hi) ? sacc[kb2][r] : kNegInf;
+        }
     }
-    if (wave_active && !empty) {
-      // ---- S^T = K Q^T: two 32-key blocks ----
-      // the two 32-key blocks are independent MFMA chains; interleave them
-      f32x16_t sacc[2];
+  };
+  // Row maximum of a score tile (log2 units, both lane halves).
+  auto tile_max = [&](const f32x16_t* sacc) {
+    float t = kNegInf;
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
+    for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kb2][r] = 0.f;
+      for (int r = 0; r < 16; ++r) t = fmaxf(t, sacc[kb2][r]);
+    return fmaxf(t, __shfl_xor(t, 32)) * a.sl;
+  };
+
+  // Software pipeline.  Iteration tt: (A) the MFMAs of S for tile tt + 1
+  // run while the VALU turns the scores of tile tt into P; (B) the MFMAs of
+  // O += P V_tt run while the VALU masks tile tt + 1 and takes its maximum,
+  // which decides the (rare) rescale applied at the top of the next
+  // iteration.  LDS holds K_{tt+1} and V_tt; K_{tt+2} and V_{tt+1} are
+  // loaded into registers at the top and stored at the bottom into the
+  // buffers of K_tt and V_{tt-1}: one barrier per tile.
+  float m_cur = kNegInf;  // maximum used for P of the current tile
+  float m_nxt = kNegInf;  // maximum for the next tile
+  bool grow = false;      // the next tile moves the maximum (wave-uniform)
+  auto iter = [&](auto cur_c, int tt, f32x16_t* s_cur, f32x16_t* s_nxt) {
+    constexpr int cur = decltype(cur_c)::value;
+    const int last = n_total - 1;
+    // rescale decided by the previous iteration
+    const float alpha = m_cur == kNegInf ? 0.f : fast_exp2(m_cur - m_nxt);
+    if (grow) {
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) {
-          const bf16x8_t kop = *reinterpret_cast<const bf16x8_t*>(kl + koff[ks] + 32 * ROW_BYTES * kb2);
-          sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[ks], sacc[kb2], 0, 0, 0);
-        }
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
+    l_run *= alpha;
+    m_cur = m_nxt;
+    load_tile(rsrc_v, lds_v[cur ^ 1], tt + 1 < last ? tt + 1 : last);
+    load_tile(rsrc_k, lds_k[cur], tt + 2 < last ? tt + 2 : last);
+
+    // ---- phase A: S of tile tt + 1 on MFMA, P of tile tt on VALU ----
+    s_tile(lds_k[cur ^ 1], s_nxt);
+    const float nm = m_cur == kNegInf ? 0.f : -m_cur;
+    u32x4_t pw[4];
+    // P of the first 32-key half here, the second half in phase B
+    auto p_half = [&](int kb2) {
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0f = fast_exp2(fmaf(s_cur[kb2][r], a.sl, nm));
+        const float p1f = fast_exp2(fmaf(s_cur[kb2][r + 1], a.sl, nm));
+        const uint32_t w = pk_bf16(p0f, p1f);
+        pw[2 * kb2 + (r >> 3)][(r & 7) >> 1] = w;
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w),
+                                                __builtin_bit_cast(bf16x2_t, one2), l_run, false);
       }
-      // ---- mask (edge tiles only): visible iff lo <= key <= hi ----
-      // key of (kb2, r) = key0 + 32 kb2 + 8 (r / 4) + 4 half + r % 4
-      if (!full) {
-        const int lo = is_sum ? -1 : tlo;
-        const int hi = is_sum ? smax : thi;
-        const int kbase = key0 + 4 * half;
+    };
+    p_half(0);
+    asm volatile("" : "+v"(pw[0]));
+    asm volatile("" : "+v"(pw[1]));
+    asm volatile("" : "+v"(l_run));
+    mask_tile(tt + 1, s_nxt);
+
+    // ---- phase B: O^T += V^T P^T on MFMA, maximum of tile tt + 1 on VALU ----
+    const char* vl = lds_v[cur];
+    p_half(1);
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, pw[ks]);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kbase + 32 * kb2 + 8 * (r >> 2) + (r & 3);
-            sacc[kb2][r] = (key >= lo && key <= hi) ? sacc[kb2][r] : kNegInf;
-          }
-      }
-      float tmax = kNegInf;
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sacc[kb2][r]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * a.sl;
-      // ---- lazy move of the reference maximum ----
-      const bool grow = tmax > m_ref + kLazyRescale;
-      if (__any(grow)) {
-        const float m_new = fmaxf(m_ref, tmax);
-        const float alpha = m_ref == kNegInf ? 0.f : fast_exp2(m_ref - m_new);
-        m_ref = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-      }
-      const float nm = m_ref == kNegInf ? 0.f : -m_ref;
-      // ---- P = exp2(s * sl - m) in bf16; the row sum adds the same
-      //      rounded values that multiply V ----
-      u32x4_t pw[4];
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0f = fast_exp2(fmaf(sacc[kb2][r], a.sl, nm));
-          const float p1f = fast_exp2(fmaf(sacc[kb2][r + 1], a.sl, nm));
-          const uint32_t w = pk_bf16(p0f, p1f);
-          pw[2 * kb2 + (r >> 3)][(r & 7) >> 1] = w;
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w),
-                                                  __builtin_bit_cast(bf16x2_t, one2), l_run, false);
-        }
-      // ---- O^T += V^T P^T ----
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, pw[ks]);
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const bf16x4_t lo = lds_read_tr(vl, voff[0][db] + 16 * ROW_BYTES * ks);
-          const bf16x4_t hi = lds_read_tr(vl, voff[1][db] + 16 * ROW_BYTES * ks);
-          const bf16x8_t vop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop, oacc[db], 0, 0, 0);
-        }
+      for (int db = 0; db < 4; ++db) {
+        const bf16x4_t lo = lds_read_tr(vl, voff[0][db] + 16 * ROW_BYTES * ks);
+        const bf16x4_t hi = lds_read_tr(vl, voff[1][db] + 16 * ROW_BYTES * ks);
+        const bf16x8_t vop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop, oacc[db], 0, 0, 0);
       }
     }
-    if (tt + 1 < n_total) KSA_STORE(cur ^ 1);
+    const float tmax = tile_max(s_nxt);
+    grow = __any(tmax > m_cur + kLazyRescale);
+    m_nxt = grow ? fmaxf(m_cur, tmax) : m_cur;
     __syncthreads();
   };
 
+  f32x16_t sa[2], sb[2];
   if (n_total > 0) {
-    KSA_PREFETCH(0);
-    KSA_STORE(0);
+    load_tile(rsrc_k, lds_k[0], 0);
+    load_tile(rsrc_v, lds_v[0], 0);
+    load_tile(rsrc_k, lds_k[1], n_total > 1 ? 1 : 0);
+    __syncthreads();
+    s_tile(lds_k[0], sa);
+    mask_tile(0, sa);
+    const float tmax = tile_max(sa);
+    grow = true;
+    m_nxt = tmax;
+    __syncthreads();
   }
-  __syncthreads();
   for (int tt = 0; tt < n_total; tt += 2) {
-    tile_step(std::integral_constant<int, 0>(), tt);
-    if (tt + 1 < n_total) tile_step(std::integral_constant<int, 1>(), tt + 1);
+    iter(std::integral_constant<int, 0>(), tt, sa, sb);
+    if (tt + 1 < n_total) iter(std::integral_constant<int, 1>(), tt + 1, sb, sa);
   }
-#undef KSA_PREFETCH
-#undef KSA_STORE
+  const float m_ref = m_cur;
 
   if (!wave_active) return;
   const float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -433,7 +486,7 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_d128_kernel(
 bool prefill_mfma_supported(const PrefillArgs& a, int32_t dtype) {
   const int g = a.hq / a.hkv;
   // 32-bit index arithmetic inside the kernel
-  const bool fits = a.L < (int64_t(1) << 30) &&
+  const bool fits = a.L < (int64_t(1) << 24) && a.L * a.hkv * D * 2 < (int64_t(1) << 31) &&
                     a.L * static_cast<int64_t>(a.hq > a.hkv ? a.hq : a.hkv) * D < (int64_t(1) << 31) &&
                     static_cast<int64_t>(a.batch) * a.hkv * g * ((a.n_text + 31) / 32) < (int64_t(1) << 31);
   return dtype == KSA_DTYPE_BF16 && a.dqk == D && a.dv == D && !a.v_is_k_prefix && fits &&
@@ -469,7 +522,8 @@ static hipError_t launch_hpw(const PrefillArgs& p, const void* q, const void* k,
   fast_div(static_cast<uint32_t>(a.k), &a.divk_m, &a.divk_l);
   a.sl = p.scale * kLog2e;
   const int64_t sum_items = static_cast<int64_t>(a.batch) * a.hkv * a.M;
-  const int64_t blocks = a.n_text_blocks + (sum_items + 3) / 4;
+  a.n_sum_blocks = static_cast<int32_t>(((sum_items + 3) / 4 + 7) / 8 * 8);  // keeps text blocks XCD-aligned
+  const int64_t blocks = a.n_text_blocks + a.n_sum_blocks;
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL(prefill_mfma_d128_kernel<HPW>, dim3(static_cast<uint32_t>(blocks)), dim3(256),
                      0, s, a, static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
