@@ -207,17 +207,14 @@ __global__ void __launch_bounds__(512, 1) decode_mla_split_kernel(
     for (int ks = 0; ks < 9; ++ks) qop[ks] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * ks);
   }
 
-  // Tile copy: lane chunk s = LOADS_PER_WAVE * 64 * wave + 64 i + lane of the
-  // tile maps to row s / 73, chunk s % 73 (chunk 72 is padding and repeats
-  // chunk 71; rows past the tile repeat its last row).  Offsets are bytes
-  // from the tile's first row.
-  // Tile copy through a buffer resource covering exactly this range's rows:
-  // a lane past the range reads zeros instead of faulting, so the last,
-  // partial tile needs no clamping.  Lane chunk s = LOADS_PER_WAVE * 64 *
-  // wave + 64 i + lane of a tile is row s / 73, 16-byte chunk s % 73 (chunk 72
-  // is row padding in LDS and just reads the next row's first chunk).
-  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<bf16_t*>(kseq), static_cast<short>(0), (r1 - r0) * (DQK * 2), 0x00020000);
+  // Tile copy through a buffer resource that starts at the tile's first row
+  // and ends with this range's last row: a lane past the range reads zeros
+  // instead of faulting (the hardware range check covers the per-lane offset
+  // only, so the tile base goes into the resource, not into soffset), and
+  // the last, partial tile needs no clamping.  Lane chunk s =
+  // LOADS_PER_WAVE * 64 * wave + 64 i + lane of a tile is row s / 73, 16-byte
+  // chunk s % 73 (chunk 72 is row padding in LDS and just reads the next
+  // row's first chunk).
   int voff[LOADS_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < LOADS_PER_WAVE; ++i) {
@@ -227,10 +224,12 @@ __global__ void __launch_bounds__(512, 1) decode_mla_split_kernel(
   }
   u32x4_t kreg[LOADS_PER_WAVE];
   auto prefetch = [&](int t) {
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<bf16_t*>(kseq + static_cast<int64_t>(t) * TK * DQK), static_cast<short>(0),
+        (r1 - r0 - t * TK) * (DQK * 2), 0x00020000);
 #pragma unroll
     for (int i = 0; i < LOADS_PER_WAVE; ++i)
-      kreg[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                rsrc, voff[i], t * TK * DQK * 2, 0));
+      kreg[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff[i], 0, 0));
   };
   auto store = [&](char* buf) {
 #pragma unroll
