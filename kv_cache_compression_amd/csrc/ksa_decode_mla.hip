@@ -8,21 +8,20 @@
 // contiguous slice (Sec. 2.3.1, Fig. 4).
 //
 // Work decomposition: the slices of all sequences are cut into row ranges of
-// about (total rows / CU count); two workgroups of 8 wavefronts (heads 0..63
-// and 64..127) handle one range, so every cache row leaves HBM once and is
-// read a second time from L2.
-//   - 32-key tiles are prefetched one tile ahead into registers with buffer
-//     loads (a lane past the range reads zeros) and stored to a double-
-//     buffered LDS tile; rows are padded to 1168 bytes so that both the MFMA
-//     operand reads (32 rows x 16 B) and the transposing reads (4 rows x
-//     32 B) are free of bank conflicts;
-//   - waves 4j .. 4j+3 own a block of 32 heads.  Wave 4j+u computes the
-//     part of S^T = K Q^T over key columns 144u .. 144u+143 on 32x32x16 bf16
-//     MFMA; the four parts are summed through LDS, all four run the same
-//     softmax, and wave 4j+u accumulates value columns 128u .. 128u+127 of
-//     O^T += V^T P^T, V^T read through ds_read_b64_tr_b16 from the same
-//     tile.  Splitting the key width as well as the value width keeps the
-//     MFMA work undivided while each wave holds a quarter of Q and of O;
+// about (total rows / CU count) rows; one workgroup of 8 wavefronts handles a
+// range for all 128 heads, so every cache row leaves HBM once.
+//   - 32-key tiles go straight from global memory into LDS (buffer_load ...
+//     lds), two tiles ahead, triple-buffered; rows are padded to 1168 bytes
+//     so that the MFMA operand reads (16 rows x 16 B) and the transposing
+//     reads (4 rows x 32 B) are free of bank conflicts; a lane past the
+//     range reads zeros, so the last, partial tile needs no clamping;
+//   - wave w owns heads 16w .. 16w+15 over the full key width: S^T = K Q^T
+//     on 16x16x32 bf16 MFMA (Q^T of its heads in registers), softmax in
+//     registers (lane = head, 8 keys per lane), and O^T += V^T P^T on the
+//     same MFMA with V^T read through ds_read_b64_tr_b16 from the same
+//     tile; P stays in the registers the scores were in, with the keys of a
+//     tile ordered to match (each lane group holds keys 4g..4g+3 and
+//     16+4g..16+4g+3);
 //   - each range writes (max, sum, unnormalised output in bf16) per head;
 //     a second kernel merges the ranges of a sequence by their maxima.
 #include <type_traits>
@@ -36,13 +35,12 @@ namespace {
 
 constexpr int DQK = 576, DV = 512;
 constexpr int HQ = 128;
-constexpr int NW = 8;                     // waves per workgroup: 2 head blocks x 4 quarters
-constexpr int HWG = 64;                   // heads per workgroup
 constexpr int TK = 32;                    // keys per tile
 constexpr int RB = DQK * 2 + 16;          // padded LDS row: 1168 bytes (73 chunks)
 constexpr int RCH = RB / 16;              // 73
-constexpr int LOADS_PER_WAVE = 5;         // 16-byte lanes: 5 x 64 x 8 = 2560 >= 32 x 73
-constexpr int TILE_LDS = NW * LOADS_PER_WAVE * 64 * 16;  // 40960 bytes
+constexpr int TILE_CH = 37 * 64;          // 16-byte chunks per tile buffer: 2368 >= 32 x 73
+constexpr int TILE_LDS = TILE_CH * 16;    // 37888 bytes
+constexpr int NBUF = 3;                   // tiles in LDS: the current one and two in flight
 constexpr float kLazy = 8.f;
 
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
@@ -173,14 +171,15 @@ __global__ void __launch_bounds__(1024) mla_plan_kernel(MlaArgs a, const int32_t
 __global__ void __launch_bounds__(512, 1) decode_mla_split_kernel(
     MlaArgs a, const bf16_t* __restrict__ ck, const int32_t* __restrict__ state,
     const bf16_t* __restrict__ q, const int32_t* __restrict__ kind, char* __restrict__ ws) {
-  __shared__ __attribute__((aligned(16))) char lds[2][TILE_LDS];
-  // partial S^T exchange: lane-major, 16 values + 4 padding per lane
-  __shared__ __attribute__((aligned(16))) float xs[NW][64][20];
-  const int hg = blockIdx.y;  // heads 64 hg .. 64 hg + 63
+  __shared__ __attribute__((aligned(16))) char lds0[TILE_LDS];
+  __shared__ __attribute__((aligned(16))) char lds1[TILE_LDS];
+  __shared__ __attribute__((aligned(16))) char lds2[TILE_LDS];
+  char* const lds[NBUF] = {lds0, lds1, lds2};
+  const int item = blockIdx.x;
   const int32_t* items = reinterpret_cast<const int32_t*>(reinterpret_cast<const MlaPlan*>(ws) + a.batch);
-  const int b = items[2 * blockIdx.x];
+  const int b = items[2 * item];
   if (b < 0) return;  // uniform over the block
-  const int sp = items[2 * blockIdx.x + 1];
+  const int sp = items[2 * item + 1];
   const MlaPlan pl = reinterpret_cast<const MlaPlan*>(ws)[b];
   const MlaSlice sl = {pl.start, pl.len};
   const int per = pl.per, nsp = pl.nsp;
@@ -191,182 +190,158 @@ __global__ void __launch_bounds__(512, 1) decode_mla_split_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int hb = wave >> 2;  // head block: heads 64 hg + 32 hb .. + 31
-  const int qu = wave & 3;   // key columns 144 qu .., value columns 128 qu ..
-  const int half = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15;  // head within the wave (S, P, O layouts) / key or d row (operands)
+  const int g4 = lane >> 4;   // 16-lane group
+  const int head = 16 * wave + l16;
   const bf16_t* kseq = ck + (static_cast<int64_t>(b) * a.slots + sl.start + r0) * DQK;
 
-  // Q^T (this wave's key-column quarter) as the B operand of S^T = K Q^T:
-  // column = head (lane % 32 of the block), k-slots d = 144 qu + 16 ks + 8 half + j.
-  bf16x8_t qop[9];
+  // Q^T as the B operand of S^T = K Q^T on 16x16x32 MFMA: column = head
+  // (lane % 16), k-slots d = 32 ks + 8 (lane / 16) + j.
+  bf16x8_t qop[18];
   {
-    const bf16_t* qp = q + (static_cast<int64_t>(b) * HQ + HWG * hg + 32 * hb + (lane & 31)) * DQK +
-                       144 * qu + 8 * half;
+    const bf16_t* qp = q + (static_cast<int64_t>(b) * HQ + head) * DQK + 8 * g4;
 #pragma unroll
-    for (int ks = 0; ks < 9; ++ks) qop[ks] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * ks);
+    for (int ks = 0; ks < 18; ++ks) qop[ks] = *reinterpret_cast<const bf16x8_t*>(qp + 32 * ks);
   }
 
-  // Tile copy through a buffer resource that starts at the tile's first row
-  // and ends with this range's last row: a lane past the range reads zeros
-  // instead of faulting (the hardware range check covers the per-lane offset
-  // only, so the tile base goes into the resource, not into soffset), and
-  // the last, partial tile needs no clamping.  Lane chunk s =
-  // LOADS_PER_WAVE * 64 * wave + 64 i + lane of a tile is row s / 73, 16-byte
-  // chunk s % 73 (chunk 72 is row padding in LDS and just reads the next
-  // row's first chunk).
-  int voff[LOADS_PER_WAVE];
+  // Tile copy straight into LDS through a buffer resource that starts at the
+  // tile's first row and ends with this range's last row (the hardware range
+  // check covers the per-lane offset only, so the tile base goes into the
+  // resource).  Chunk s = 64 (8 i + wave) + lane of a tile (i < 5,
+  // 8 i + wave < 37) is row s / 73, 16-byte chunk s % 73; chunk 72 is row
+  // padding in LDS and just reads the next row's first chunk.
+  const int nld = wave < 5 ? 5 : 4;
+  int voff[5];
 #pragma unroll
-  for (int i = 0; i < LOADS_PER_WAVE; ++i) {
-    const int s_ = (LOADS_PER_WAVE * wave + i) * 64 + lane;
+  for (int i = 0; i < 5; ++i) {
+    const int s_ = (8 * i + wave) * 64 + lane;
     const int row = s_ / RCH;
     voff[i] = row * (DQK * 2) + 16 * (s_ - row * RCH);
   }
-  u32x4_t kreg[LOADS_PER_WAVE];
-  auto prefetch = [&](int t) {
+  auto prefetch = [&](int t, char* buf) __attribute__((always_inline)) {
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<bf16_t*>(kseq + static_cast<int64_t>(t) * TK * DQK), static_cast<short>(0),
         (r1 - r0 - t * TK) * (DQK * 2), 0x00020000);
 #pragma unroll
-    for (int i = 0; i < LOADS_PER_WAVE; ++i)
-      kreg[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff[i], 0, 0));
-  };
-  auto store = [&](char* buf) {
-#pragma unroll
-    for (int i = 0; i < LOADS_PER_WAVE; ++i)
-      *reinterpret_cast<u32x4_t*>(buf + (LOADS_PER_WAVE * wave + i) * 1024 + 16 * lane) = kreg[i];
+    for (int i = 0; i < 5; ++i)
+      if (i < nld)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsrc, (__attribute__((address_space(3))) void*)(buf + (8 * i + wave) * 1024), 16, voff[i], 0, 0, 0);
   };
 
-  f32x16_t oacc[4];
+  // O^T (d x heads) in 32 blocks of 16 d: lane holds head lane % 16,
+  // d = 16 blk + 4 (lane / 16) + r.
+  f32x4_t oacc[32];
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+  for (int i = 0; i < 32; ++i) oacc[i] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
   float m_ref = kNegInf, l_run = 0.f;
-  const uint32_t one2 = 0x3f803f80u;
 
-  // per-lane LDS offsets
-  const int krow_off = (lane & 31) * RB + 16 * half + 288 * qu;
-  const int G = lane >> 4, l16 = lane & 15, rr = l16 >> 2, c4 = l16 & 3;
-  const int vrow_off = (4 * (G >> 1) + rr) * RB + 2 * (16 * (G & 1) + 4 * c4) + 256 * qu;
+  // K operand (A of S^T): row = key 16 kb + lane % 16, bytes 64 ks + 16 (lane / 16).
+  const int krow_off = l16 * RB + 16 * g4;
+  // V^T operand (A of O^T += V^T P^T): the k-slots of lane group g are keys
+  // 4g .. 4g+3 and 16+4g .. 16+4g+3 (the order in which the S^T layout holds
+  // P); a transposing read over rows 4g + (lane % 16) / 4 and d = 16 blk +
+  // 4 (lane % 4) gives lane i of the group V[4 keys][16 blk + i].
+  const int vrow_off = (4 * g4 + (l16 >> 2)) * RB + 2 * (4 * (l16 & 3));
 
-  if (ntile > 0) {
-    prefetch(0);
-    store(lds[0]);
-  }
-  __syncthreads();
-  auto tile_step = [&](auto cur_c, int t) {
+  if (ntile > 0) prefetch(0, lds[0]);
+  if (ntile > 1) prefetch(1, lds[1]);
+  auto tile_step = [&](auto cur_c, int t) __attribute__((always_inline)) {
     constexpr int cur = decltype(cur_c)::value;
-    if (t + 1 < ntile) prefetch(t + 1);  // in flight during this tile
+    if (t + 1 < ntile) {
+      if (wave < 5)
+        __builtin_amdgcn_s_waitcnt(0x0075);  // vmcnt(5) lgkmcnt(0)
+      else
+        __builtin_amdgcn_s_waitcnt(0x0074);  // vmcnt(4) lgkmcnt(0)
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+    }
+    wg_barrier();
+    if (t + 2 < ntile) prefetch(t + 2, lds[(cur + 2) % NBUF]);
     const char* kl = lds[cur];
 
-    // ---- this wave's quarter of S^T = K Q^T ----
-    // three independent accumulation chains keep the MFMA pipe busy
-    f32x16_t s, s1, s2;
+    // ---- S^T = K Q^T: keys 0..15 and 16..31, two chains each ----
+    f32x4_t s0a = {0.f, 0.f, 0.f, 0.f}, s0b = s0a, s1a = s0a, s1b = s0a;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = s1[r] = s2[r] = 0.f;
-    {
-      bf16x8_t kop[9];  // all operand reads issued before the MFMAs
-#pragma unroll
-      for (int ks = 0; ks < 9; ++ks) kop[ks] = *reinterpret_cast<const bf16x8_t*>(kl + krow_off + 32 * ks);
-#pragma unroll
-      for (int ks = 0; ks < 9; ks += 3) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qop[ks], s, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks + 1], qop[ks + 1], s1, 0, 0, 0);
-        s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks + 2], qop[ks + 2], s2, 0, 0, 0);
-      }
+    for (int ks = 0; ks < 18; ks += 2) {
+      const bf16x8_t k0a = *reinterpret_cast<const bf16x8_t*>(kl + krow_off + 64 * ks);
+      const bf16x8_t k1a = *reinterpret_cast<const bf16x8_t*>(kl + krow_off + 16 * RB + 64 * ks);
+      const bf16x8_t k0b = *reinterpret_cast<const bf16x8_t*>(kl + krow_off + 64 * (ks + 1));
+      const bf16x8_t k1b = *reinterpret_cast<const bf16x8_t*>(kl + krow_off + 16 * RB + 64 * (ks + 1));
+      s0a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0a, qop[ks], s0a, 0, 0, 0);
+      s1a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1a, qop[ks], s1a, 0, 0, 0);
+      s0b = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0b, qop[ks + 1], s0b, 0, 0, 0);
+      s1b = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1b, qop[ks + 1], s1b, 0, 0, 0);
     }
+    // lane: head lane % 16; sv[r] = key 4 g + r, sv[4 + r] = key 16 + 4 g + r
+    float sv[8];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] += s1[r] + s2[r];
-#pragma unroll
-    for (int r = 0; r < 16; r += 4)
-      *reinterpret_cast<f32x4_t*>(&xs[wave][lane][r]) = (f32x4_t){s[r], s[r + 1], s[r + 2], s[r + 3]};
-    // exchange written (lgkmcnt(0)); the prefetch stays in flight, so a bare
-    // s_barrier rather than __syncthreads
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-    wg_barrier();
-    {
-      f32x4_t part[3][4];
-#pragma unroll
-      for (int o = 1; o < 4; ++o)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          part[o - 1][r] = *reinterpret_cast<const f32x4_t*>(&xs[(wave & ~3) | ((qu + o) & 3)][lane][4 * r]);
-#pragma unroll
-      for (int o = 0; o < 3; ++o)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] += part[o][r >> 2][r & 3];
+    for (int r = 0; r < 4; ++r) {
+      sv[r] = s0a[r] + s0b[r];
+      sv[4 + r] = s1a[r] + s1b[r];
     }
-    // ---- softmax: lane = head, registers = keys 8 (r/4) + 4 half + r%4 ----
     const int valid = (r1 - r0) - t * TK;
     if (valid < TK) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        s[r] = (8 * (r >> 2) + 4 * half + (r & 3)) < valid ? s[r] : kNegInf;
+      for (int j = 0; j < 8; ++j) sv[j] = (4 * g4 + (j & 3) + 16 * (j >> 2)) < valid ? sv[j] : kNegInf;
     }
     float tmax = kNegInf;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[r]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * a.sl;
+    for (int j = 0; j < 8; ++j) tmax = fmaxf(tmax, sv[j]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    tmax *= a.sl;
     if (__any(tmax > m_ref + kLazy)) {
       const float m_new = fmaxf(m_ref, tmax);
       const float alpha = m_ref == kNegInf ? 0.f : fast_exp2(m_ref - m_new);
       m_ref = m_new;
       l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      for (int i = 0; i < 32; ++i) oacc[i] *= alpha;
     }
     const float nm = m_ref == kNegInf ? 0.f : -m_ref;
-    u32x4_t pw[2];
+    u32x4_t pw;
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const uint32_t w = pk_bf16(fast_exp2(fmaf(s[r], a.sl, nm)), fast_exp2(fmaf(s[r + 1], a.sl, nm)));
-      pw[r >> 3][(r & 7) >> 1] = w;
+    for (int j = 0; j < 8; j += 2) {
+      const uint32_t w = pk_bf16(fast_exp2(fmaf(sv[j], a.sl, nm)), fast_exp2(fmaf(sv[j + 1], a.sl, nm)));
+      pw[j >> 1] = w;
       l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w),
-                                              __builtin_bit_cast(bf16x2_t, one2), l_run, false);
+                                              __builtin_bit_cast(bf16x2_t, 0x3f803f80u), l_run, false);
     }
-    // ---- this wave's quarter of O^T += V^T P^T (V = first 512 key columns) ----
+    const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, pw);
+    // ---- O^T += V^T P^T over 32 blocks of 16 value columns ----
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, pw[ks]);
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const int off = vrow_off + 16 * ks * RB + 64 * db;
-        const bf16x4_t lo = lds_read_tr(kl, off);
-        const bf16x4_t hi = lds_read_tr(kl, off + 8 * RB);
-        const bf16x8_t vop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop, oacc[db], 0, 0, 0);
-      }
+    for (int blk = 0; blk < 32; ++blk) {
+      const bf16x4_t lo = lds_read_tr(kl, vrow_off + 32 * blk);
+      const bf16x4_t hi = lds_read_tr(kl, vrow_off + 16 * RB + 32 * blk);
+      const bf16x8_t vop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      oacc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop, oacc[blk], 0, 0, 0);
     }
-    if (t + 1 < ntile) store(lds[cur ^ 1]);
-    __syncthreads();
   };
-  for (int t = 0; t < ntile; t += 2) {
+  for (int t = 0; t < ntile; t += 3) {
     tile_step(std::integral_constant<int, 0>(), t);
     if (t + 1 < ntile) tile_step(std::integral_constant<int, 1>(), t + 1);
+    if (t + 2 < ntile) tile_step(std::integral_constant<int, 2>(), t + 2);
   }
+  __builtin_amdgcn_s_waitcnt(0x0070);  // no LDS write in flight at exit
 
-  // ---- write this range's partial (the four quarters hold the same m and l) ----
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const int head = HWG * hg + 32 * hb + (lane & 31);
-  char* rec = ws + mla_plan_bytes(a.batch) + ((static_cast<int64_t>(blockIdx.x)) * HQ + head) * kMlaRec;
-  if (half == 0 && qu == 0) {
+  // ---- this range's partial: {m, l} and the unnormalised output (bf16) ----
+  float l_tot = l_run + __shfl_xor(l_run, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  char* rec = ws + mla_plan_bytes(a.batch) + ((static_cast<int64_t>(item)) * HQ + head) * kMlaRec;
+  if (g4 == 0) {
     reinterpret_cast<float*>(rec)[0] = m_ref;
     reinterpret_cast<float*>(rec)[1] = l_tot;
   }
-  bf16_t* ro = reinterpret_cast<bf16_t*>(rec + 8) + 128 * qu;
+  bf16_t* ro = reinterpret_cast<bf16_t*>(rec + 8);
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-      const int d = 32 * db + 8 * qq + 4 * half;
-      u32x2_t w;
-      w.x = pk_bf16(oacc[db][4 * qq + 0], oacc[db][4 * qq + 1]);
-      w.y = pk_bf16(oacc[db][4 * qq + 2], oacc[db][4 * qq + 3]);
-      *reinterpret_cast<u32x2_t*>(ro + d) = w;
-    }
+  for (int blk = 0; blk < 32; ++blk) {
+    u32x2_t w;
+    w.x = pk_bf16(oacc[blk][0], oacc[blk][1]);
+    w.y = pk_bf16(oacc[blk][2], oacc[blk][3]);
+    *reinterpret_cast<u32x2_t*>(ro + 16 * blk + 4 * g4) = w;
+  }
 }
 
 __global__ void __launch_bounds__(256) decode_mla_merge_kernel(MlaArgs a,
@@ -447,14 +422,15 @@ hipError_t launch_decode_mla(const DecodeArgs& d, const void* ck, const int32_t*
   a.smax = 0;
   a.sl = d.scale * kLog2e;
   int dev = 0, ncu = 256;
-  if (hipGetDevice(&dev) == hipSuccess)
-    hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    ncu = 256;
   a.n_cu = ncu > 0 ? (ncu < kMlaCuCap ? ncu : kMlaCuCap) : 256;
   hipLaunchKernelGGL(mla_plan_kernel, dim3(1), dim3(((d.batch + 63) / 64) * 64), 0, s, a, state, kind,
                      static_cast<MlaPlan*>(ws));
   hipError_t e0 = hipGetLastError();
   if (e0 != hipSuccess) return e0;
-  hipLaunchKernelGGL(decode_mla_split_kernel, dim3(a.n_cu + d.batch, HQ / HWG), dim3(512), 0, s, a,
+  hipLaunchKernelGGL(decode_mla_split_kernel, dim3(a.n_cu + d.batch), dim3(512), 0, s, a,
                      static_cast<const bf16_t*>(ck), state, static_cast<const bf16_t*>(q), kind,
                      static_cast<char*>(ws));
   hipError_t e = hipGetLastError();
