@@ -368,13 +368,7 @@ hipError_t launch_decode(const DecodeArgs& a, int32_t dtype, const void* ck, con
                          const int32_t* state, const void* q, const int32_t* kind, void* out,
                          float* lse, void* ws, hipStream_t s) {
   int32_t* st = const_cast<int32_t*>(state);
-  if (decode_mla_supported(a, dtype)) {
-    hipLaunchKernelGGL(decode_check_kernel, dim3((a.batch + 255) / 256), dim3(256), 0, s, a.batch,
-                       a.k, a.C, a.max_summaries, st, kind);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return launch_decode_mla(a, ck, state, q, kind, out, lse, ws, s);
-  }
+  if (decode_mla_supported(a, dtype)) return launch_decode_mla(a, ck, st, q, kind, out, lse, ws, s);
   if (!gqa_fast_ok(a, dtype)) {
     if (dtype == KSA_DTYPE_FP32)
       return launch_decode_generic<float>(a, ck, cv, st, q, kind, out, lse, s);

@@ -9,21 +9,26 @@
 //
 // Work decomposition: the slices of all sequences are cut into row ranges of
 // about (total rows / CU count) rows; one workgroup of 8 wavefronts handles a
-// range for all 128 heads, so every cache row leaves HBM once.
+// range for all 128 heads, so every cache row leaves HBM once.  Every
+// workgroup derives the cut itself from the cache states (a few lanes of
+// arithmetic per sequence), so the decode is two launches: split and merge.
 //   - 32-key tiles go straight from global memory into LDS (buffer_load ...
 //     lds), two tiles ahead, triple-buffered; rows are padded to 1168 bytes
-//     so that the MFMA operand reads (16 rows x 16 B) and the transposing
-//     reads (4 rows x 32 B) are free of bank conflicts; a lane past the
-//     range reads zeros, so the last, partial tile needs no clamping;
-//   - wave w owns heads 16w .. 16w+15 over the full key width: S^T = K Q^T
-//     on 16x16x32 bf16 MFMA (Q^T of its heads in registers), softmax in
-//     registers (lane = head, 8 keys per lane), and O^T += V^T P^T on the
-//     same MFMA with V^T read through ds_read_b64_tr_b16 from the same
-//     tile; P stays in the registers the scores were in, with the keys of a
-//     tile ordered to match (each lane group holds keys 4g..4g+3 and
-//     16+4g..16+4g+3);
+//     so that both the MFMA operand reads (32 rows x 16 B) and the
+//     transposing reads (4 rows x 32 B) are free of bank conflicts; a lane
+//     past the range reads zeros, so the last, partial tile needs no
+//     clamping;
+//   - waves 2p and 2p+1 own heads 32p .. 32p+31.  Wave 2p+h computes the
+//     part of S^T = K Q^T over key columns 288h .. 288h+287 on 32x32x16 bf16
+//     MFMA; the two parts are summed through LDS, both waves run the same
+//     softmax, and wave 2p+h accumulates value columns 256h .. 256h+255 of
+//     O^T += V^T P^T, V^T read through ds_read_b64_tr_b16 from the same
+//     tile.  Splitting the key width as well as the value width keeps the
+//     MFMA work undivided while each wave holds half of Q and of O, and
+//     halves the LDS operand traffic of one wave per 16 heads;
 //   - each range writes (max, sum, unnormalised output in bf16) per head;
-//     a second kernel merges the ranges of a sequence by their maxima.
+//     the merge kernel combines the ranges of a sequence by their maxima and
+//     flags sequences whose slice cannot be read.
 #include <type_traits>
 
 #include "ksa_common.h"
@@ -68,105 +73,106 @@ __device__ __forceinline__ bf16x4_t lds_read_tr(const char* base, int byte_off) 
 }
 
 struct MlaArgs {
-  int32_t batch, k, C, max_summaries, smax, n_cu;
+  int32_t batch, k, C, max_summaries, n_cu, max_items;
   int64_t slots;
   float sl;  // scale * log2(e)
 };
 
 struct MlaSlice {
   int32_t start, len;
+  bool ok;
 };
 
+// The slice of one sequence (Sec. 2.3.1): text queries read the current
+// chunk, the ring and the summaries that left the window; summary queries
+// read the scratch slot and the current chunk.  A slice that cannot be read
+// (a summary query without a committed chunk, a state out of range) has
+// length 0.
 __device__ __forceinline__ MlaSlice mla_slice(const MlaArgs& a, const int32_t* state, int kind) {
   const int m = state[0], r = state[1];
   MlaSlice s;
   if (kind == 0) {
-    const bool ok = r >= 0 && r <= a.k && m >= 0 && m <= a.max_summaries;
+    s.ok = r >= 0 && r <= a.k && m >= 0 && m <= a.max_summaries;
     s.start = 1 + a.k - r;
-    s.len = ok ? r + (m < a.C ? m : a.C) * a.k + (m > a.C ? m - a.C : 0) : 0;
-  } else if (kind == 1) {
-    const bool ok = r == 0 && m >= 1 && m <= a.max_summaries;
-    s.start = 0;
-    s.len = ok ? a.k + 1 : 0;
+    s.len = s.ok ? r + (m < a.C ? m : a.C) * a.k + (m > a.C ? m - a.C : 0) : 0;
   } else {
+    s.ok = r == 0 && m >= 1 && m <= a.max_summaries;  // the summary was just committed
     s.start = 0;
-    s.len = 0;
+    s.len = s.ok ? a.k + 1 : 0;
   }
   return s;
 }
 
-// Per-sequence plan, computed once per call by mla_plan_kernel:
-// {slice start, slice length, rows per range, number of ranges}, followed
-// by a work list of (sequence, range) pairs, one per split workgroup.
-struct MlaPlan {
-  int32_t start, len, per, nsp, first, pad0, pad1, pad2;  // first: index of its first work item
+__device__ __forceinline__ int seq_len(const MlaArgs& a, const int32_t* state, const int32_t* kind, int b) {
+  return (b < a.batch && kind[b] >= 0) ? mla_slice(a, state + 4 * b, kind[b]).len : 0;
+}
+
+// Rows per range: about total / (CU count - batch), at least 64, a whole
+// number of tiles; with it the ranges of all sequences number at most the CU
+// count.  Every lane of the calling wave gets the same value.
+__device__ int mla_per(const MlaArgs& a, const int32_t* state, const int32_t* kind) {
+  const int lane = threadIdx.x & 63;
+  int64_t total = 0;
+  for (int b0 = 0; b0 < a.batch; b0 += 64) {
+    int64_t v = seq_len(a, state, kind, b0 + lane);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    total += v;
+  }
+  const int64_t slots = a.n_cu - a.batch > a.n_cu / 2 ? a.n_cu - a.batch : a.n_cu / 2;
+  int64_t per = (total + slots - 1) / slots;
+  if (per < 64) per = 64;
+  return static_cast<int>((per + TK - 1) / TK * TK);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
+// Work item `item` of the cut: ranges are numbered sequence by sequence;
+// b = -1 when the item is past the last range.
+struct MlaItem {
+  int32_t b, sp, start, len, per;
 };
 
-constexpr int kMlaCuCap = 1024;  // CU counts above this are clamped
+__device__ MlaItem mla_item(const MlaArgs& a, const int32_t* state, const int32_t* kind, int item) {
+  const int lane = threadIdx.x & 63;
+  const int per = mla_per(a, state, kind);
+  MlaItem it = {-1, 0, 0, 0, per};
+  int first = 0;  // ranges of the sequences before this 64-sequence chunk
+  for (int b0 = 0; b0 < a.batch; b0 += 64) {
+    const int b = b0 + lane;
+    const int len = seq_len(a, state, kind, b);
+    const int nsp = (len + per - 1) / per;
+    const int incl = wave_scan(nsp);
+    const bool mine = item >= first + incl - nsp && item < first + incl;
+    const uint64_t hit = __ballot(mine);
+    if (hit) {
+      const int src = __builtin_ctzll(hit);
+      it.b = __shfl(b, src);
+      it.sp = item - first - (__shfl(incl, src) - __shfl(nsp, src));
+      it.len = __shfl(len, src);
+      it.start = (b < a.batch && kind[b] >= 0) ? mla_slice(a, state + 4 * b, kind[b]).start : 0;
+      it.start = __shfl(it.start, src);
+      return it;
+    }
+    first += __shfl(incl, 63);
+  }
+  return it;
+}
 
 }  // namespace
 
-// Record of one (sequence, range, head): {m (log2 units), l} as two floats,
-// then 512 bf16 of the unnormalised output.  The workspace starts with the
-// per-sequence plans (256-byte aligned), then the records.
+// Record of one (work item, head): {m (log2 units), l} as two floats, then
+// 512 bf16 of the unnormalised output.
 constexpr int kMlaRec = 8 + DV * 2;
-
-// Work-list capacity: with ranges of ceil(total / n_cu) rows there are at
-// most n_cu + batch of them.
-__host__ __device__ __forceinline__ int mla_max_items(int batch) { return kMlaCuCap + batch; }
-
-__host__ __device__ __forceinline__ size_t mla_plan_bytes(int batch) {
-  return (static_cast<size_t>(batch) * sizeof(MlaPlan) + sizeof(int32_t) * 2 * mla_max_items(batch) + 255) /
-         256 * 256;
-}
-
-// Cut every slice into ranges of about (total rows / CU count) rows, at least
-// 64, and list the (sequence, range) work items.  One workgroup, one thread
-// per sequence (batch <= 1024).
-__global__ void __launch_bounds__(1024) mla_plan_kernel(MlaArgs a, const int32_t* __restrict__ state,
-                                                        const int32_t* __restrict__ kind,
-                                                        MlaPlan* __restrict__ plan) {
-  __shared__ int64_t part[1024 / 64];
-  const int b = threadIdx.x;
-  MlaSlice sl = {0, 0};
-  if (b < a.batch && kind[b] >= 0) sl = mla_slice(a, state + 4 * b, kind[b]);
-  int64_t v = sl.len;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  if ((b & 63) == 0) part[b >> 6] = v;
-  __syncthreads();
-  int64_t total = 0;
-  for (int w = 0; w < (static_cast<int>(blockDim.x) + 63) / 64; ++w) total += part[w];
-  // ranges of total / (n_cu - batch) rows give at most n_cu ranges, so the
-  // two head groups fill exactly two rounds of workgroups
-  const int64_t slots = a.n_cu - a.batch > a.n_cu / 2 ? a.n_cu - a.batch : a.n_cu / 2;
-  int64_t target = (total + slots - 1) / slots;
-  if (target < 64) target = 64;
-  target = (target + TK - 1) / TK * TK;
-  __shared__ int32_t nsp_s[1024];
-  MlaPlan pl;
-  pl.start = sl.start;
-  pl.len = sl.len;
-  pl.per = static_cast<int32_t>(target);
-  pl.nsp = static_cast<int32_t>((sl.len + target - 1) / target);
-  nsp_s[b] = b < a.batch ? pl.nsp : 0;
-  __syncthreads();
-  // work list: item i -> (sequence, range); unused items get sequence -1
-  int32_t* items = reinterpret_cast<int32_t*>(plan + a.batch);
-  if (b < a.batch) {
-    int first = 0;
-    for (int i = 0; i < b; ++i) first += nsp_s[i];
-    pl.first = first;
-    plan[b] = pl;
-    for (int r = 0; r < pl.nsp; ++r) {
-      items[2 * (first + r)] = b;
-      items[2 * (first + r) + 1] = r;
-    }
-  }
-  int used = 0;
-  for (int i = 0; i < a.batch; ++i) used += nsp_s[i];
-  for (int i = used + b; i < mla_max_items(a.batch); i += blockDim.x) items[2 * i] = -1;
-}
 
 __global__ void __launch_bounds__(512, 1) decode_mla_split_kernel(
     MlaArgs a, const bf16_t* __restrict__ ck, const int32_t* __restrict__ state,
@@ -174,35 +180,37 @@ __global__ void __launch_bounds__(512, 1) decode_mla_split_kernel(
   __shared__ __attribute__((aligned(16))) char lds0[TILE_LDS];
   __shared__ __attribute__((aligned(16))) char lds1[TILE_LDS];
   __shared__ __attribute__((aligned(16))) char lds2[TILE_LDS];
+  // partial S^T exchange between the two waves of a pair: 16 values + 4
+  // padding per lane
+  __shared__ __attribute__((aligned(16))) float xs[8][64][20];
   char* const lds[NBUF] = {lds0, lds1, lds2};
-  const int item = blockIdx.x;
-  const int32_t* items = reinterpret_cast<const int32_t*>(reinterpret_cast<const MlaPlan*>(ws) + a.batch);
-  const int b = items[2 * item];
+  const MlaItem it = mla_item(a, state, kind, blockIdx.x);
+  // wave-uniform: keep them in scalar registers
+  const int b = __builtin_amdgcn_readfirstlane(it.b);
   if (b < 0) return;  // uniform over the block
-  const int sp = items[2 * item + 1];
-  const MlaPlan pl = reinterpret_cast<const MlaPlan*>(ws)[b];
-  const MlaSlice sl = {pl.start, pl.len};
-  const int per = pl.per, nsp = pl.nsp;
-  if (sp >= nsp) return;  // uniform over the block
-  const int r0 = sp * per;
-  const int r1 = r0 + per < sl.len ? r0 + per : sl.len;
+  const int per = __builtin_amdgcn_readfirstlane(it.per);
+  const int len = __builtin_amdgcn_readfirstlane(it.len);
+  const int start = __builtin_amdgcn_readfirstlane(it.start);
+  const int r0 = __builtin_amdgcn_readfirstlane(it.sp) * per;
+  const int r1 = r0 + per < len ? r0 + per : len;
   const int ntile = (r1 - r0 + TK - 1) / TK;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l16 = lane & 15;  // head within the wave (S, P, O layouts) / key or d row (operands)
-  const int g4 = lane >> 4;   // 16-lane group
-  const int head = 16 * wave + l16;
-  const bf16_t* kseq = ck + (static_cast<int64_t>(b) * a.slots + sl.start + r0) * DQK;
+  const int pair = wave >> 1;  // heads 32 pair .. 32 pair + 31
+  const int hf = wave & 1;     // key columns 288 hf .., value columns 256 hf ..
+  const int half = lane >> 5;
+  const int head = 32 * pair + (lane & 31);
+  const bf16_t* kseq = ck + (static_cast<int64_t>(b) * a.slots + start + r0) * DQK;
 
-  // Q^T as the B operand of S^T = K Q^T on 16x16x32 MFMA: column = head
-  // (lane % 16), k-slots d = 32 ks + 8 (lane / 16) + j.
+  // Q^T (this wave's key-column half) as the B operand of S^T = K Q^T on
+  // 32x32x16 MFMA: column = head (lane % 32), k-slots d = 288 hf + 16 ks + 8 half + j.
   bf16x8_t qop[18];
   {
-    const bf16_t* qp = q + (static_cast<int64_t>(b) * HQ + head) * DQK + 8 * g4;
+    const bf16_t* qp = q + (static_cast<int64_t>(b) * HQ + head) * DQK + 288 * hf + 8 * half;
 #pragma unroll
-    for (int ks = 0; ks < 18; ++ks) qop[ks] = *reinterpret_cast<const bf16x8_t*>(qp + 32 * ks);
+    for (int ks = 0; ks < 18; ++ks) qop[ks] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * ks);
   }
 
   // Tile copy straight into LDS through a buffer resource that starts at the
@@ -230,20 +238,24 @@ __global__ void __launch_bounds__(512, 1) decode_mla_split_kernel(
             rsrc, (__attribute__((address_space(3))) void*)(buf + (8 * i + wave) * 1024), 16, voff[i], 0, 0, 0);
   };
 
-  // O^T (d x heads) in 32 blocks of 16 d: lane holds head lane % 16,
-  // d = 16 blk + 4 (lane / 16) + r.
-  f32x4_t oacc[32];
+  // O^T over this wave's 256 value columns in 8 blocks of 32: lane holds
+  // head lane % 32, d = 256 hf + 32 db + 8 (r / 4) + 4 half + r % 4.
+  f32x16_t oacc[8];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) oacc[i] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  for (int db = 0; db < 8; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
   float m_ref = kNegInf, l_run = 0.f;
+  const uint32_t one2 = 0x3f803f80u;
 
-  // K operand (A of S^T): row = key 16 kb + lane % 16, bytes 64 ks + 16 (lane / 16).
-  const int krow_off = l16 * RB + 16 * g4;
-  // V^T operand (A of O^T += V^T P^T): the k-slots of lane group g are keys
-  // 4g .. 4g+3 and 16+4g .. 16+4g+3 (the order in which the S^T layout holds
-  // P); a transposing read over rows 4g + (lane % 16) / 4 and d = 16 blk +
-  // 4 (lane % 4) gives lane i of the group V[4 keys][16 blk + i].
-  const int vrow_off = (4 * g4 + (l16 >> 2)) * RB + 2 * (4 * (l16 & 3));
+  // K operand: row = key lane % 32, bytes 576 hf + 32 ks + 16 half.
+  const int krow_off = (lane & 31) * RB + 16 * half + 576 * hf;
+  // V^T operand: in 16-lane group G, lane (4 rr + c4) reads key row
+  // 4 (G / 2) + rr (+ 8 for the second half of the k-slots) and d =
+  // 256 hf + 32 db + 16 (G % 2) + 4 c4; the transposing read gives lane i
+  // V[4 keys][d = 256 hf + 32 db + i % 32].
+  const int G = lane >> 4, l16 = lane & 15, rr = l16 >> 2, c4 = l16 & 3;
+  const int vrow_off = (4 * (G >> 1) + rr) * RB + 2 * (16 * (G & 1) + 4 * c4) + 512 * hf;
 
   if (ntile > 0) prefetch(0, lds[0]);
   if (ntile > 1) prefetch(1, lds[1]);
@@ -258,65 +270,76 @@ __global__ void __launch_bounds__(512, 1) decode_mla_split_kernel(
       __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
     }
     wg_barrier();
-    if (t + 2 < ntile) prefetch(t + 2, lds[(cur + 2) % NBUF]);
     const char* kl = lds[cur];
 
-    // ---- S^T = K Q^T: keys 0..15 and 16..31, two chains each ----
-    f32x4_t s0a = {0.f, 0.f, 0.f, 0.f}, s0b = s0a, s1a = s0a, s1b = s0a;
+    // ---- this wave's half of S^T = K Q^T (keys x heads, 32 x 32) ----
+    f32x16_t s;
 #pragma unroll
-    for (int ks = 0; ks < 18; ks += 2) {
-      const bf16x8_t k0a = *reinterpret_cast<const bf16x8_t*>(kl + krow_off + 64 * ks);
-      const bf16x8_t k1a = *reinterpret_cast<const bf16x8_t*>(kl + krow_off + 16 * RB + 64 * ks);
-      const bf16x8_t k0b = *reinterpret_cast<const bf16x8_t*>(kl + krow_off + 64 * (ks + 1));
-      const bf16x8_t k1b = *reinterpret_cast<const bf16x8_t*>(kl + krow_off + 16 * RB + 64 * (ks + 1));
-      s0a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0a, qop[ks], s0a, 0, 0, 0);
-      s1a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1a, qop[ks], s1a, 0, 0, 0);
-      s0b = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0b, qop[ks + 1], s0b, 0, 0, 0);
-      s1b = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1b, qop[ks + 1], s1b, 0, 0, 0);
-    }
-    // lane: head lane % 16; sv[r] = key 4 g + r, sv[4 + r] = key 16 + 4 g + r
-    float sv[8];
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      sv[r] = s0a[r] + s0b[r];
-      sv[4 + r] = s1a[r] + s1b[r];
+    for (int ks = 0; ks < 18; ++ks) {
+      const bf16x8_t kop = *reinterpret_cast<const bf16x8_t*>(kl + krow_off + 32 * ks);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[ks], s, 0, 0, 0);
     }
+#pragma unroll
+    for (int r = 0; r < 16; r += 4)
+      *reinterpret_cast<f32x4_t*>(&xs[wave][lane][r]) = (f32x4_t){s[r], s[r + 1], s[r + 2], s[r + 3]};
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // exchange written (lgkmcnt(0)); loads stay in flight
+    wg_barrier();
+    {
+      f32x4_t part[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) part[r] = *reinterpret_cast<const f32x4_t*>(&xs[wave ^ 1][lane][4 * r]);
+      // the same sum in both waves of the pair: a + b == b + a exactly
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = hf == 0 ? s[r] + part[r >> 2][r & 3] : part[r >> 2][r & 3] + s[r];
+    }
+    // tile t + 2 goes into the buffer of tile t - 1 (released by the barrier
+    // at the top of this iteration); issued after the exchange reads so that
+    // they do not wait for it
+    if (t + 2 < ntile) prefetch(t + 2, lds[(cur + 2) % NBUF]);
+    // ---- softmax: lane = head, registers = keys 8 (r/4) + 4 half + r%4 ----
     const int valid = (r1 - r0) - t * TK;
     if (valid < TK) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) sv[j] = (4 * g4 + (j & 3) + 16 * (j >> 2)) < valid ? sv[j] : kNegInf;
+      for (int r = 0; r < 16; ++r)
+        s[r] = (8 * (r >> 2) + 4 * half + (r & 3)) < valid ? s[r] : kNegInf;
     }
     float tmax = kNegInf;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) tmax = fmaxf(tmax, sv[j]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    tmax *= a.sl;
+    for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[r]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * a.sl;
     if (__any(tmax > m_ref + kLazy)) {
       const float m_new = fmaxf(m_ref, tmax);
       const float alpha = m_ref == kNegInf ? 0.f : fast_exp2(m_ref - m_new);
       m_ref = m_new;
       l_run *= alpha;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) oacc[i] *= alpha;
+      for (int db = 0; db < 8; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
     }
     const float nm = m_ref == kNegInf ? 0.f : -m_ref;
-    u32x4_t pw;
+    u32x4_t pw[2];
 #pragma unroll
-    for (int j = 0; j < 8; j += 2) {
-      const uint32_t w = pk_bf16(fast_exp2(fmaf(sv[j], a.sl, nm)), fast_exp2(fmaf(sv[j + 1], a.sl, nm)));
-      pw[j >> 1] = w;
+    for (int r = 0; r < 16; r += 2) {
+      const uint32_t w = pk_bf16(fast_exp2(fmaf(s[r], a.sl, nm)), fast_exp2(fmaf(s[r + 1], a.sl, nm)));
+      pw[r >> 3][(r & 7) >> 1] = w;
       l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w),
-                                              __builtin_bit_cast(bf16x2_t, 0x3f803f80u), l_run, false);
+                                              __builtin_bit_cast(bf16x2_t, one2), l_run, false);
     }
-    const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, pw);
-    // ---- O^T += V^T P^T over 32 blocks of 16 value columns ----
+    // ---- this wave's half of O^T += V^T P^T (V = first 512 key columns) ----
 #pragma unroll
-    for (int blk = 0; blk < 32; ++blk) {
-      const bf16x4_t lo = lds_read_tr(kl, vrow_off + 32 * blk);
-      const bf16x4_t hi = lds_read_tr(kl, vrow_off + 16 * RB + 32 * blk);
-      const bf16x8_t vop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      oacc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop, oacc[blk], 0, 0, 0);
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, pw[ks]);
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const int off = vrow_off + 16 * ks * RB + 64 * db;
+        const bf16x4_t lo = lds_read_tr(kl, off);
+        const bf16x4_t hi = lds_read_tr(kl, off + 8 * RB);
+        const bf16x8_t vop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop, oacc[db], 0, 0, 0);
+      }
     }
   };
   for (int t = 0; t < ntile; t += 3) {
@@ -326,25 +349,29 @@ __global__ void __launch_bounds__(512, 1) decode_mla_split_kernel(
   }
   __builtin_amdgcn_s_waitcnt(0x0070);  // no LDS write in flight at exit
 
-  // ---- this range's partial: {m, l} and the unnormalised output (bf16) ----
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-  char* rec = ws + mla_plan_bytes(a.batch) + ((static_cast<int64_t>(item)) * HQ + head) * kMlaRec;
-  if (g4 == 0) {
+  // ---- this range's partial (both waves of a pair hold the same m and l) ----
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  char* rec = ws + (static_cast<int64_t>(blockIdx.x) * HQ + head) * kMlaRec;
+  if (half == 0 && hf == 0) {
     reinterpret_cast<float*>(rec)[0] = m_ref;
     reinterpret_cast<float*>(rec)[1] = l_tot;
   }
-  bf16_t* ro = reinterpret_cast<bf16_t*>(rec + 8);
+  bf16_t* ro = reinterpret_cast<bf16_t*>(rec + 8) + 256 * hf;
 #pragma unroll
-  for (int blk = 0; blk < 32; ++blk) {
-    u32x2_t w;
-    w.x = pk_bf16(oacc[blk][0], oacc[blk][1]);
-    w.y = pk_bf16(oacc[blk][2], oacc[blk][3]);
-    *reinterpret_cast<u32x2_t*>(ro + 16 * blk + 4 * g4) = w;
-  }
+  for (int db = 0; db < 8; ++db)
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const int d = 32 * db + 8 * qq + 4 * half;
+      u32x2_t w;
+      w.x = pk_bf16(oacc[db][4 * qq + 0], oacc[db][4 * qq + 1]);
+      w.y = pk_bf16(oacc[db][4 * qq + 2], oacc[db][4 * qq + 3]);
+      *reinterpret_cast<u32x2_t*>(ro + d) = w;
+    }
 }
 
-__global__ void __launch_bounds__(256) decode_mla_merge_kernel(MlaArgs a,
+// One block per (head, sequence): combine the ranges of the sequence by
+// their maxima; the head-0 block also flags a slice that cannot be read.
+__global__ void __launch_bounds__(256) decode_mla_merge_kernel(MlaArgs a, int32_t* __restrict__ state,
                                                                const int32_t* __restrict__ kind,
                                                                const char* __restrict__ ws,
                                                                bf16_t* __restrict__ out,
@@ -352,13 +379,37 @@ __global__ void __launch_bounds__(256) decode_mla_merge_kernel(MlaArgs a,
   const int head = blockIdx.x;
   const int b = blockIdx.y;
   if (kind[b] < 0) return;
-  const MlaPlan pl = reinterpret_cast<const MlaPlan*>(ws)[b];
-  const int nsp = pl.nsp;
-  const char* rec0 = ws + mla_plan_bytes(a.batch) + (static_cast<int64_t>(pl.first) * HQ + head) * kMlaRec;
-  const int64_t stride = static_cast<int64_t>(HQ) * kMlaRec;
-  // weights of every range, computed once per block into LDS
   __shared__ float wgt[256];
   __shared__ float red[2];
+  __shared__ int seq[2];  // first range of the sequence, number of ranges
+  if (threadIdx.x < 64) {
+    // the cut, as the split kernel derived it
+    const int lane = threadIdx.x;
+    const int per = mla_per(a, state, kind);
+    int first = 0, nsp_b = 0;
+    for (int b0 = 0; b0 < a.batch; b0 += 64) {
+      const int bb = b0 + lane;
+      const int nsp = (seq_len(a, state, kind, bb) + per - 1) / per;
+      const int incl = wave_scan(nsp);
+      if (b >= b0 && b < b0 + 64) {
+        const int src = b - b0;
+        first += __shfl(incl, src) - __shfl(nsp, src);
+        nsp_b = __shfl(nsp, src);
+        break;
+      }
+      first += __shfl(incl, 63);
+    }
+    if (lane == 0) {
+      seq[0] = first;
+      seq[1] = nsp_b;
+      if (head == 0 && !mla_slice(a, state + 4 * b, kind[b]).ok) state[4 * b + 3] |= KSA_CACHE_ERR_BAD_SUMMARY_READ;
+    }
+  }
+  __syncthreads();
+  const int nsp = seq[1];
+  const char* rec0 = ws + (static_cast<int64_t>(seq[0]) * HQ + head) * kMlaRec;
+  const int64_t stride = static_cast<int64_t>(HQ) * kMlaRec;
+  // weights of every range, computed once per block into LDS
   if (threadIdx.x < 64) {
     float mloc = kNegInf;
     for (int s = threadIdx.x; s < nsp; s += 64)
@@ -384,34 +435,47 @@ __global__ void __launch_bounds__(256) decode_mla_merge_kernel(MlaArgs a,
   const float mx = red[0], l = red[1];
   const float mu = mx == kNegInf ? 0.f : mx;
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  for (int d = 2 * threadIdx.x; d < DV; d += 2 * blockDim.x) {
-    float o0 = 0.f, o1 = 0.f;
-    for (int s = 0; s < nsp; ++s) {
-      const char* r = rec0 + s * stride;
-      const float w = s < 256 ? wgt[s] : fast_exp2(reinterpret_cast<const float*>(r)[0] - mu);
-      const uint32_t v = *reinterpret_cast<const uint32_t*>(r + 8 + 2 * d);
-      o0 += w * __uint_as_float(v << 16);
-      o1 += w * __uint_as_float(v & 0xffff0000u);
+  const int d = 2 * threadIdx.x;  // 256 threads x 2 columns = 512
+  float o0 = 0.f, o1 = 0.f;
+  // four ranges' loads in flight at a time
+  int s = 0;
+  for (; s + 4 <= nsp; s += 4) {
+    uint32_t v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const uint32_t*>(rec0 + (s + u) * stride + 8 + 2 * d);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float w = s + u < 256 ? wgt[s + u]
+                                  : fast_exp2(reinterpret_cast<const float*>(rec0 + (s + u) * stride)[0] - mu);
+      o0 += w * __uint_as_float(v[u] << 16);
+      o1 += w * __uint_as_float(v[u] & 0xffff0000u);
     }
-    *reinterpret_cast<uint32_t*>(out + (static_cast<int64_t>(b) * HQ + head) * DV + d) =
-        pk_bf16(o0 * inv, o1 * inv);
   }
+  for (; s < nsp; ++s) {
+    const char* r = rec0 + s * stride;
+    const float w = s < 256 ? wgt[s] : fast_exp2(reinterpret_cast<const float*>(r)[0] - mu);
+    const uint32_t v = *reinterpret_cast<const uint32_t*>(r + 8 + 2 * d);
+    o0 += w * __uint_as_float(v << 16);
+    o1 += w * __uint_as_float(v & 0xffff0000u);
+  }
+  *reinterpret_cast<uint32_t*>(out + (static_cast<int64_t>(b) * HQ + head) * DV + d) = pk_bf16(o0 * inv, o1 * inv);
   if (lse && threadIdx.x == 0)
     lse[static_cast<int64_t>(b) * HQ + head] = l > 0.f ? (mx + log2f(l)) * kLn2 : kNegInf;
 }
 
 bool decode_mla_supported(const DecodeArgs& a, int32_t dtype) {
   return dtype == KSA_DTYPE_BF16 && a.v_is_k_prefix && a.dqk == DQK && a.dv == DV && a.hq == HQ &&
-         a.hkv == 1 && a.batch <= 1024 && a.slots < (int64_t(1) << 31) / DQK;
+         a.hkv == 1 && a.slots < (int64_t(1) << 31) / DQK;
 }
 
+// At most CU count + batch work items (the cut above), whatever the device.
+static constexpr int kMlaCuCap = 1024;
 
 size_t decode_mla_workspace_bytes(const DecodeArgs& a) {
-  const size_t plan = mla_plan_bytes(a.batch);
-  return plan + static_cast<size_t>(kMlaCuCap + a.batch) * HQ * kMlaRec;
+  return static_cast<size_t>(kMlaCuCap + a.batch) * HQ * kMlaRec;
 }
 
-hipError_t launch_decode_mla(const DecodeArgs& d, const void* ck, const int32_t* state, const void* q,
+hipError_t launch_decode_mla(const DecodeArgs& d, const void* ck, int32_t* state, const void* q,
                              const int32_t* kind, void* out, float* lse, void* ws, hipStream_t s) {
   MlaArgs a;
   a.batch = d.batch;
@@ -419,24 +483,22 @@ hipError_t launch_decode_mla(const DecodeArgs& d, const void* ck, const int32_t*
   a.C = d.C;
   a.max_summaries = d.max_summaries;
   a.slots = d.slots;
-  a.smax = 0;
   a.sl = d.scale * kLog2e;
   int dev = 0, ncu = 256;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     ncu = 256;
   a.n_cu = ncu > 0 ? (ncu < kMlaCuCap ? ncu : kMlaCuCap) : 256;
-  hipLaunchKernelGGL(mla_plan_kernel, dim3(1), dim3(((d.batch + 63) / 64) * 64), 0, s, a, state, kind,
-                     static_cast<MlaPlan*>(ws));
-  hipError_t e0 = hipGetLastError();
-  if (e0 != hipSuccess) return e0;
-  hipLaunchKernelGGL(decode_mla_split_kernel, dim3(a.n_cu + d.batch), dim3(512), 0, s, a,
-                     static_cast<const bf16_t*>(ck), state, static_cast<const bf16_t*>(q), kind,
-                     static_cast<char*>(ws));
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_mla_merge_kernel, dim3(HQ, d.batch), dim3(256), 0, s, a, kind,
-                     static_cast<const char*>(ws), static_cast<bf16_t*>(out), lse);
+  a.max_items = a.n_cu + d.batch;
+  if (d.batch > 0) {
+    hipLaunchKernelGGL(decode_mla_split_kernel, dim3(a.max_items), dim3(512), 0, s, a,
+                       static_cast<const bf16_t*>(ck), state, static_cast<const bf16_t*>(q), kind,
+                       static_cast<char*>(ws));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_mla_merge_kernel, dim3(HQ, d.batch), dim3(256), 0, s, a, state, kind,
+                       static_cast<const char*>(ws), static_cast<bf16_t*>(out), lse);
+  }
   return hipGetLastError();
 }
 

@@ -65,7 +65,7 @@ size_t decode_workspace_bytes(const DecodeArgs& a);
 // absorbed-MLA split-K decode: bf16, Hq = 128, Hkv = 1, Dqk = 576, Dv = 512
 bool decode_mla_supported(const DecodeArgs& a, int32_t dtype);
 size_t decode_mla_workspace_bytes(const DecodeArgs& a);
-hipError_t launch_decode_mla(const DecodeArgs& a, const void* ck, const int32_t* state, const void* q,
+hipError_t launch_decode_mla(const DecodeArgs& a, const void* ck, int32_t* state, const void* q,
                              const int32_t* kind, void* out, float* lse, void* ws, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int32_t dtype, const void* ck, const void* cv,
                          const int32_t* state, const void* q, const int32_t* kind, void* out,
