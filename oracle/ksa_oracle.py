@@ -255,6 +255,82 @@ def token_swa_mask(n: int, k: int, W: int) -> np.ndarray:
     return out
 
 
+MODE_KSA, MODE_SCA, MODE_SWA = 0, 1, 2
+
+
+def baseline_mask(n: int, k: int, mode: int, C: int = 0, W: int = 0,
+                  rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Visibility of the summary-free baselines the report compares KSA with
+    (Fig. 3; the Hybrid-SCA / Hybrid-SWA rows of its comparisons), laid over
+    the same Eq. 1 sequence so that inputs and outputs keep one layout.
+
+    ``MODE_SCA`` (sliding chunk attention): text t_i, c = floor(i/k), sees
+    the text t_{(c-C)k} .. t_i (clamped at 0) and no summary.
+    ``MODE_SWA`` (token sliding window of W tokens): text t_i sees the text
+    t_{i-W+1} .. t_i (clamped at 0) and no summary.
+    ``MODE_KSA`` is :func:`visibility_mask_fast`.
+    Summary rows keep the KSA rule in every mode: s_j sees its chunk and
+    itself.  These modes are a reading of the baselines (the report gives
+    no kernel for them); the window sizes are parameters.
+    """
+    if mode == MODE_KSA:
+        return visibility_mask_fast(n, k, C, rows=rows)
+    is_s, idx = augmented_rows(n, k)
+    rows = np.arange(len(is_s)) if rows is None else np.asarray(rows, dtype=np.int64)
+    qs = is_s[rows][:, None]
+    qi = idx[rows][:, None]
+    ks = is_s[None, :]
+    ki = idx[None, :]
+    if mode == MODE_SCA:
+        text_q = ~ks & (ki // k >= qi // k - C) & (ki <= qi)
+    elif mode == MODE_SWA:
+        if W < 1:
+            raise ValueError("token window must hold at least the query")
+        text_q = ~ks & (ki >= qi - W + 1) & (ki <= qi)
+    else:
+        raise ValueError(f"unknown mode {mode}")
+    summ_q = (~ks & (ki // k == qi)) | (ks & (ki == qi))
+    return np.where(qs, summ_q, text_q)
+
+
+def baseline_pairs_closed_form(n: int, k: int, mode: int, C: int = 0, W: int = 0) -> int:
+    """Visible pairs of one head under :func:`baseline_mask`, counted row by
+    row from the window sizes: text t_i sees min(floor(i/k), C) k + i mod k + 1
+    keys (SCA) or min(i + 1, W) keys (SWA); each summary sees k + 1."""
+    M = n // k
+    tot = M * (k + 1)
+    for i in range(n):
+        if mode == MODE_SCA:
+            tot += min(i // k, C) * k + i % k + 1
+        else:
+            tot += min(i + 1, W)
+    return tot
+
+
+def baseline_attention(q: np.ndarray, kx: np.ndarray, v: Optional[np.ndarray], n: int, k: int,
+                       mode: int, scale: float, C: int = 0, W: int = 0,
+                       rows: Optional[Sequence[int]] = None, dv: Optional[int] = None,
+                       row_block: int = 512) -> Tuple[np.ndarray, np.ndarray]:
+    """Eq. 10 (masked softmax attention) under :func:`baseline_mask`, in fp64;
+    same shapes and conventions as :func:`ksa_attention`."""
+    L = augmented_len(n, k)
+    rows = np.arange(L) if rows is None else np.asarray(rows, dtype=np.int64)
+    if v is None:
+        v = kx[..., :dv]
+    Hq, Hkv = q.shape[1], kx.shape[1]
+    g = Hq // Hkv
+    out = np.zeros((len(rows), Hq, v.shape[-1]))
+    lse = np.zeros((Hq, len(rows)))
+    for b0 in range(0, len(rows), row_block):
+        rb = rows[b0:b0 + row_block]
+        mask = baseline_mask(n, k, mode, C, W, rows=rb)
+        for h in range(Hq):
+            o, l_ = attention_masked(q[rb, h], kx[:, h // g], v[:, h // g], mask, scale)
+            out[b0:b0 + len(rb), h] = o
+            lse[h, b0:b0 + len(rb)] = l_
+    return out, lse
+
+
 def visible_pairs_bruteforce(n: int, k: int, C: int,
                              summary_sees_self: bool = True) -> int:
     return int(visibility_mask_fast(n, k, C, summary_sees_self).sum())
