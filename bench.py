@@ -65,6 +65,17 @@ def visible_pairs(n: int, k: int, C: int) -> int:
     return tot
 
 
+def baseline_pairs(n: int, k: int, mode: int, C: int, W: int) -> int:
+    """Visible (query, key) pairs of one head for the summary-free baselines:
+    text t_i sees min(floor(i/k), C) k + i mod k + 1 keys (sliding chunks) or
+    min(i + 1, W) keys (token window); every summary row sees k + 1."""
+    import numpy as np
+
+    i = np.arange(n, dtype=np.int64)
+    text = np.minimum(i // k, C) * k + i % k + 1 if mode == 1 else np.minimum(i + 1, W)
+    return int(text.sum()) + (n // k) * (k + 1)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -205,6 +216,21 @@ def main() -> int:
         if any(errs):
             raise RuntimeError(f"decode cache error bits {errs}")
     long_runs = [] if args.no_long else prefill_long(ksa, ksa_synth, torch, dev, stream)
+    # the report's summary-free baselines on the same inputs (A/B timing)
+    modes = []
+    for mode, name, W in ((ksa.MODE_SCA, "sliding chunks (no summaries)", 0),
+                          (ksa.MODE_SWA, f"token window of {w.window * w.chunk}", w.window * w.chunk)):
+        ksa.ksa_prefill_attn_mode(p, mode, W, qd, kd, vd, w.n_text, out=out, stream=stream)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(5):
+            ksa.ksa_prefill_attn_mode(p, mode, W, qd, kd, vd, w.n_text, out=out, stream=stream)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / 5
+        fl = 2 * (w.dqk + w.dv) * w.hq * baseline_pairs(w.n_text, w.chunk, mode, w.window, W) * w.batch
+        modes.append({"mode": name, "ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+                      "ksa_ms": round(seg_ms["prefill"], 4)})
 
     pre_tflops = flops / (seg_ms["prefill"] * 1e-3) / 1e12
     dec_gbps = dec_bytes / (seg_ms["decode"] * 1e-3) / 1e9
@@ -242,6 +268,7 @@ def main() -> int:
                        "ms": round(seg_ms["decode_mla"], 4), "workload": mw.name,
                        "slice_rows_total": mla_rows, "bytes": mla_bytes},
         "prefill_long": long_runs,
+        "prefill_baselines": modes,
         "rope": {"value": round(rope_gbps, 1), "unit": "GB/s", "ms": round(seg_ms["rope"], 4)},
         "breakdown_ms": {s: round(v, 4) for s, v in seg_ms.items()},
         "roofline": {"kernel": "prefill_mfma_d128_kernel", "bound": "mfma", "achieved": round(pre_tflops, 2),

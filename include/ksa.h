@@ -135,6 +135,25 @@ KSA_API int32_t ksa_rope_positions(const ksa_params* p, int64_t rows, const int6
 KSA_API int32_t ksa_prefill_attn(const ksa_params* p, int32_t batch, int64_t n_text, const void* q,
                          const void* k, const void* v, void* out, float* lse, void* stream);
 
+/* Summary-free baselines the report compares KSA with (Fig. 3; the
+ * Hybrid-SCA / Hybrid-SWA comparisons), laid over the same Eq. 1 layout so
+ * that the same inputs can be timed against KSA:
+ *   KSA_MODE_KSA  the KSA rule (same as ksa_prefill_attn);
+ *   KSA_MODE_SCA  sliding chunk attention: text t_i (c = i / k) sees text
+ *                 t_{max(0,(c-C)k)} .. t_i and no summary;
+ *   KSA_MODE_SWA  token sliding window: text t_i sees text
+ *                 t_{max(0,i-W+1)} .. t_i and no summary, W = window_tokens.
+ * Summary rows keep the KSA rule (own chunk and itself) in every mode. */
+enum { KSA_MODE_KSA = 0, KSA_MODE_SCA = 1, KSA_MODE_SWA = 2 };
+
+/* ksa_prefill_attn with a visibility mode.  window_tokens (W >= 1) is used
+ * by KSA_MODE_SWA only.  Same shapes, kernels and errors as
+ * ksa_prefill_attn; an unknown mode or W < 1 with SWA is
+ * KSA_STATUS_INVALID_ARGUMENT. */
+KSA_API int32_t ksa_prefill_attn_mode(const ksa_params* p, int32_t mode, int64_t window_tokens, int32_t batch,
+                              int64_t n_text, const void* q, const void* k, const void* v, void* out,
+                              float* lse, void* stream);
+
 /* Slots per (sequence, kv head): 1 + k + C*k + max_summaries; -1 on bad input. */
 KSA_API int64_t ksa_cache_slots(const ksa_params* p, int32_t max_summaries);
 

@@ -33,7 +33,7 @@ KSA_CACHE_ERR_BAD_SUMMARY_READ = 8
 # Every symbol the header declares.
 EXPORTS = (
     "ksa_status_string", "ksa_last_error_message", "ksa_augmented_len", "ksa_rope_augmented",
-    "ksa_rope_positions", "ksa_prefill_attn", "ksa_cache_slots", "ksa_cache_reset",
+    "ksa_rope_positions", "ksa_prefill_attn", "ksa_prefill_attn_mode", "ksa_cache_slots", "ksa_cache_reset",
     "ksa_cache_append", "ksa_cache_fill", "ksa_decode_workspace_bytes", "ksa_decode_attn",
     "ksa_cache_read_errors",
 )
@@ -87,6 +87,7 @@ _SIGS = {
     "ksa_rope_augmented": (_i32, [_P, _i32, _i64, _vp, _i32, _i32, _i32, _i32, ctypes.c_double, _vp]),
     "ksa_rope_positions": (_i32, [_P, _i64, _vp, _vp, _i32, _i32, _i32, _i32, ctypes.c_double, _vp]),
     "ksa_prefill_attn": (_i32, [_P, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "ksa_prefill_attn_mode": (_i32, [_P, _i32, _i64, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
     "ksa_cache_slots": (_i64, [_P, _i32]),
     "ksa_cache_reset": (_i32, [_P, _C, _i32, _vp]),
     "ksa_cache_append": (_i32, [_P, _C, _i32, _vp, _vp, _vp, _vp]),
@@ -199,10 +200,10 @@ def ksa_rope_positions(p: Params, x: torch.Tensor, positions: torch.Tensor, thet
                                     rot_dim, float(theta), _stream(stream)))
 
 
-def ksa_prefill_attn(p: Params, q: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tensor],
-                     n_text: int, out: Optional[torch.Tensor] = None,
-                     lse: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """KSA prefill over the augmented sequence.  Returns ``out`` [B, L, Hq, Dv]."""
+MODE_KSA, MODE_SCA, MODE_SWA = 0, 1, 2
+
+
+def _prefill_buffers(p: Params, q, k, v, n_text: int, out, lse):
     B = q.shape[0]
     L = ksa_augmented_len(n_text, p.chunk_size)
     _need(q, (B, L, p.num_q_heads, p.head_dim_qk), p.dtype, "q")
@@ -214,10 +215,31 @@ def ksa_prefill_attn(p: Params, q: torch.Tensor, k: torch.Tensor, v: Optional[to
     _need(out, (B, L, p.num_q_heads, p.head_dim_v), p.dtype, "out")
     if lse is not None:
         _need(lse, (B, p.num_q_heads, L), torch.float32, "lse")
+    return B, out
+
+
+def ksa_prefill_attn(p: Params, q: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tensor],
+                     n_text: int, out: Optional[torch.Tensor] = None,
+                     lse: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """KSA prefill over the augmented sequence.  Returns ``out`` [B, L, Hq, Dv]."""
+    B, out = _prefill_buffers(p, q, k, v, n_text, out, lse)
     pc = p.c()
     _check(lib().ksa_prefill_attn(ctypes.byref(pc), B, n_text, _ptr(q), _ptr(k),
                                   None if p.v_is_k_prefix else _ptr(v), _ptr(out), _ptr(lse),
                                   _stream(stream)))
+    return out
+
+
+def ksa_prefill_attn_mode(p: Params, mode: int, window_tokens: int, q: torch.Tensor, k: torch.Tensor,
+                          v: Optional[torch.Tensor], n_text: int, out: Optional[torch.Tensor] = None,
+                          lse: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Prefill with a visibility mode (MODE_KSA, MODE_SCA, MODE_SWA with a
+    window of ``window_tokens``).  Returns ``out`` [B, L, Hq, Dv]."""
+    B, out = _prefill_buffers(p, q, k, v, n_text, out, lse)
+    pc = p.c()
+    _check(lib().ksa_prefill_attn_mode(ctypes.byref(pc), mode, window_tokens, B, n_text, _ptr(q), _ptr(k),
+                                       None if p.v_is_k_prefix else _ptr(v), _ptr(out), _ptr(lse),
+                                       _stream(stream)))
     return out
 
 

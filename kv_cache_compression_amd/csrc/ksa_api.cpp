@@ -162,9 +162,14 @@ int32_t ksa_rope_positions(const ksa_params* p, int64_t rows, const int64_t* pos
   return rope_common(p, ra, x, stream);
 }
 
-int32_t ksa_prefill_attn(const ksa_params* p, int32_t batch, int64_t n_text, const void* q,
-                         const void* k, const void* v, void* out, float* lse, void* stream) {
+int32_t ksa_prefill_attn_mode(const ksa_params* p, int32_t mode, int64_t window_tokens, int32_t batch,
+                              int64_t n_text, const void* q, const void* k, const void* v, void* out,
+                              float* lse, void* stream) {
   if (int32_t st = check_params(p)) return st;
+  if (mode != KSA_MODE_KSA && mode != KSA_MODE_SCA && mode != KSA_MODE_SWA)
+    return fail(KSA_STATUS_INVALID_ARGUMENT, "unknown prefill mode");
+  if (mode == KSA_MODE_SWA && window_tokens < 1)
+    return fail(KSA_STATUS_INVALID_ARGUMENT, "token window must be at least 1");
   if (batch < 0 || n_text < 0) return fail(KSA_STATUS_INVALID_ARGUMENT, "negative batch/n_text");
   if (n_text > (int64_t(1) << 40)) return fail(KSA_STATUS_UNSUPPORTED, "n_text too large");
   if (batch == 0 || n_text == 0) return KSA_STATUS_OK;
@@ -182,11 +187,19 @@ int32_t ksa_prefill_attn(const ksa_params* p, int32_t batch, int64_t n_text, con
   a.dv = p->head_dim_v;
   a.v_is_k_prefix = p->v_is_k_prefix;
   a.scale = p->softmax_scale;
+  a.mode = mode;
+  // a window wider than the sequence is the whole causal prefix
+  a.window_tokens = mode == KSA_MODE_SWA ? (window_tokens < n_text ? window_tokens : n_text) : 0;
   g_msg[0] = 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (ksa::prefill_mfma_supported(a, p->dtype))
     return hip_status(ksa::launch_prefill_mfma_d128(a, q, k, v, out, lse, s), "prefill");
   return hip_status(ksa::launch_prefill_generic(a, p->dtype, 0, q, k, v, out, lse, s), "prefill");
+}
+
+int32_t ksa_prefill_attn(const ksa_params* p, int32_t batch, int64_t n_text, const void* q,
+                         const void* k, const void* v, void* out, float* lse, void* stream) {
+  return ksa_prefill_attn_mode(p, KSA_MODE_KSA, 0, batch, n_text, q, k, v, out, lse, stream);
 }
 
 int64_t ksa_cache_slots(const ksa_params* p, int32_t max_summaries) {

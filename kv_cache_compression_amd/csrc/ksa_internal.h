@@ -27,6 +27,8 @@ struct PrefillArgs {
   int32_t k, C, hq, hkv, dqk, dv;
   int32_t v_is_k_prefix;
   float scale;
+  int32_t mode;           // KSA_MODE_*
+  int64_t window_tokens;  // W of KSA_MODE_SWA
 };
 
 // Generic prefill over a subset of augmented rows: rows_kind selects

@@ -7,6 +7,8 @@
 //   summary s_j:               its chunk's text and itself, which are the k+1
 //                              consecutive augmented rows j(k+1) .. j(k+1)+k.
 // No mask is formed: the two runs above are enumerated from chunk indices.
+// The summary-free baseline modes drop the summary run (SCA) or also replace
+// the text run by the last W tokens (SWA).
 #include "ksa_attend_wave.h"
 #include "ksa_internal.h"
 
@@ -57,11 +59,14 @@ __global__ void __launch_bounds__(256) prefill_generic_kernel(PrefillArgs a, int
   } else {
     const int64_t i = row < M * (a.k + 1) ? c * a.k + o : M * a.k + (row - M * (a.k + 1));
     const int64_t ci = i / a.k;
-    for (int64_t j = 0; j < ci - a.C; ++j) {
+    // summaries that left the window (KSA only)
+    const int64_t ns = a.mode == KSA_MODE_KSA ? ci - a.C : 0;
+    for (int64_t j = 0; j < ns; ++j) {
       const int64_t r = summary_row(j, a.k);
       wave_attn_step<T, NQ, NV>(st, kbase + r * kstride, vbase + r * vstride, a.dqk, a.dv, lane);
     }
-    const int64_t t0 = ci - a.C > 0 ? (ci - a.C) * a.k : 0;
+    int64_t t0 = ci - a.C > 0 ? (ci - a.C) * a.k : 0;  // chunk window (KSA, SCA)
+    if (a.mode == KSA_MODE_SWA) t0 = i - a.window_tokens + 1 > 0 ? i - a.window_tokens + 1 : 0;
     for (int64_t t = t0; t <= i; ++t) {
       const int64_t r = text_row(t, a.k);
       wave_attn_step<T, NQ, NV>(st, kbase + r * kstride, vbase + r * vstride, a.dqk, a.dv, lane);

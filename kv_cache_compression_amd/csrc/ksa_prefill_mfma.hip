@@ -64,6 +64,8 @@ struct MfmaArgs {
   int32_t n_tiles, n_hg, xcd_map, n_text_blocks, n_sum_blocks;
   uint32_t divk_m, divk_l;  // floor(t / k) = (umulhi(t, m) + t) >> l for t < 2^31
   float sl;                 // softmax scale * log2(e)
+  int32_t mode;             // KSA_MODE_*: summaries and text window of text queries
+  int32_t W;                // token window of KSA_MODE_SWA
 };
 
 __device__ __forceinline__ int32_t div_k(const MfmaArgs& a, int32_t t) {
@@ -221,8 +223,11 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_d128_kernel(
   const int p0 = tile * PT;
   const int p_last = (p0 + PT < a.n ? p0 + PT : a.n) - 1;
   const int c_first = div_k(a, p0), c_last = div_k(a, p_last);
-  const int sn = c_last - a.C > 0 ? c_last - a.C : 0;           // summaries s_0 .. s_{sn-1}
-  const int t0 = c_first - a.C > 0 ? (c_first - a.C) * a.k : 0;  // text t0 .. p_last
+  // summaries s_0 .. s_{sn-1} and text t0 .. p_last; the summary-free
+  // baselines have no summary run, SWA a token window instead of a chunk one
+  const int sn = a.mode == KSA_MODE_KSA && c_last - a.C > 0 ? c_last - a.C : 0;
+  const int t0 = a.mode == KSA_MODE_SWA ? (p0 - a.W + 1 > 0 ? p0 - a.W + 1 : 0)
+                                        : (c_first - a.C > 0 ? (c_first - a.C) * a.k : 0);
   const int ns = (sn + BN - 1) / BN;
   const int n_total = ns + (p_last - t0 + BN) / BN;
 
@@ -234,10 +239,13 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_d128_kernel(
   const bool q_valid = qi < a.n;
   const int ci = div_k(a, q_valid ? qi : 0);
   const int smax = q_valid ? ci - a.C - 1 : -1;                       // summaries j <= smax
-  const int tlo = q_valid ? (ci - a.C > 0 ? (ci - a.C) * a.k : 0) : 0x7fffffff;
+  // first visible text key of this lane's query and of the wave's last query
+  auto text_lo = [&](int i, int c) { return a.mode == KSA_MODE_SWA ? (i - a.W + 1 > 0 ? i - a.W + 1 : 0)
+                                                                    : (c - a.C > 0 ? (c - a.C) * a.k : 0); };
+  const int tlo = q_valid ? text_lo(qi, ci) : 0x7fffffff;
   const int thi = qi;
   const int cw0 = div_k(a, wave_active ? iw0 : 0), cw1 = div_k(a, wave_active ? iw1 : 0);
-  const int tlo_w1 = cw1 - a.C > 0 ? (cw1 - a.C) * a.k : 0;
+  const int tlo_w1 = text_lo(wave_active ? iw1 : 0, cw1);
 
   // Q^T as the B operand: column = query (lane % 32), k-slots
   // d = 16 ks + 8 (lane / 32) + j.
@@ -521,6 +529,8 @@ static hipError_t launch_hpw(const PrefillArgs& p, const void* q, const void* k,
   a.xcd_map = (n_slots % 8) == 0 ? 1 : 0;
   fast_div(static_cast<uint32_t>(a.k), &a.divk_m, &a.divk_l);
   a.sl = p.scale * kLog2e;
+  a.mode = p.mode;
+  a.W = static_cast<int32_t>(p.window_tokens);
   const int64_t sum_items = static_cast<int64_t>(a.batch) * a.hkv * a.M;
   a.n_sum_blocks = static_cast<int32_t>(((sum_items + 3) / 4 + 7) / 8 * 8);  // keeps text blocks XCD-aligned
   const int64_t blocks = a.n_text_blocks + a.n_sum_blocks;

@@ -30,7 +30,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(L):
     decl = _declared()
-    assert len(decl) == 13
+    assert len(decl) == 14
     assert sorted(K.EXPORTS) == decl
     for name in decl:
         assert hasattr(L, name), name
@@ -81,6 +81,19 @@ def test_invalid_arguments_rejected_before_launch(L):
     rc, _ = _status(L, L.ksa_prefill_attn(ctypes.byref(bad), 1, 512, fake, fake, None, fake, None, None))
     assert rc == 1
     assert L.ksa_prefill_attn(ctypes.byref(p), 0, 512, None, None, None, None, None, None) == 0
+
+
+def test_prefill_mode_arguments(L):
+    p = _params()
+    fake = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    rc, msg = _status(L, L.ksa_prefill_attn_mode(ctypes.byref(p), 3, 0, 1, 512, fake, fake, fake, fake, None, None))
+    assert rc == 1 and "mode" in msg
+    rc, msg = _status(L, L.ksa_prefill_attn_mode(ctypes.byref(p), 2, 0, 1, 512, fake, fake, fake, fake, None, None))
+    assert rc == 1 and "window" in msg
+    rc, _ = _status(L, L.ksa_prefill_attn_mode(ctypes.byref(p), 1, 0, 1, 512, fake, fake, None, fake, None, None))
+    assert rc == 1  # v missing
+    for mode in (0, 1, 2):
+        assert L.ksa_prefill_attn_mode(ctypes.byref(p), mode, 5, 0, 512, None, None, None, None, None, None) == 0
 
 
 def test_cache_argument_checks(L):
