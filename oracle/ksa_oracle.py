@@ -18,6 +18,8 @@ reordering beyond what the definitions state:
 * masked softmax attention ...... Sec. 4.1.4, Eq. (9) and Eq. (10)
 * KV-cache layout and lifecycle . Sec. 2.3.1 and Fig. 4 (a)-(e)
 * per-token cache accounting .... Sec. 3, Table 1, Eq. (4)-(6)
+* attention backward ............ chain rule through Eq. (10) (the report
+  trains with this kernel, Sec. 2.3); the softmax Jacobian written out
 
 Readings taken where the pages are silent or ambiguous (each one is listed,
 with its reason, in the design notes at the repository root):
@@ -329,6 +331,64 @@ def baseline_attention(q: np.ndarray, kx: np.ndarray, v: Optional[np.ndarray], n
             out[b0:b0 + len(rb), h] = o
             lse[h, b0:b0 + len(rb)] = l_
     return out, lse
+
+
+def attention_masked_backward(q: np.ndarray, kx: np.ndarray, v: np.ndarray, mask: np.ndarray,
+                              scale: float, dout: np.ndarray
+                              ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Gradients of O = softmax(scale * q k^T + M) v (one head, Eq. 10) with
+    respect to q, k and v, given dL/dO = ``dout``, in fp64.
+
+    Straight chain rule: with P the masked softmax, dV = P^T dO and
+    dP = dO v^T; each row of P goes through the softmax Jacobian
+    diag(p) - p p^T, so dS_i = p_i * dP_i - p_i (p_i . dP_i); then
+    dq = scale dS k and dk = scale dS^T q.  Hidden pairs have p = 0 and get
+    no gradient.  Returns (dq [R, Dqk], dk [L, Dqk], dv [L, Dv]).
+    """
+    q = q.astype(np.float64)
+    kx = kx.astype(np.float64)
+    v = v.astype(np.float64)
+    g = dout.astype(np.float64)
+    s = np.where(mask, (q @ kx.T) * scale, -np.inf)
+    mx = s.max(axis=1, keepdims=True)
+    if not np.all(np.isfinite(mx)):
+        raise ValueError("a query row sees no key")
+    p = np.exp(s - mx)
+    p /= p.sum(axis=1, keepdims=True)
+    dv = p.T @ g
+    dp = g @ v.T
+    ds = p * dp - p * (p * dp).sum(axis=1, keepdims=True)
+    return scale * (ds @ kx), scale * (ds.T @ q), dv
+
+
+def attention_backward(q: np.ndarray, kx: np.ndarray, v: np.ndarray, dout: np.ndarray,
+                       n: int, k: int, scale: float, mode: int = MODE_KSA, C: int = 0,
+                       W: int = 0, row_block: int = 512
+                       ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Backward of the prefill attention over the whole augmented sequence
+    (Eq. 10 under the KSA mask of Sec. 2.2, or a baseline mask).
+
+    q [L, Hq, Dqk], kx [L, Hkv, Dqk], v [L, Hkv, Dv], dout [L, Hq, Dv].
+    Query head h reads kv head h // (Hq/Hkv), so dk and dv of a kv head sum
+    the contributions of every query head in its group.  Returns
+    (dq [L, Hq, Dqk], dk [L, Hkv, Dqk], dv [L, Hkv, Dv]) in fp64.
+    """
+    L, Hq, _ = q.shape
+    Hkv = kx.shape[1]
+    g = Hq // Hkv
+    dq = np.zeros(q.shape)
+    dk = np.zeros(kx.shape)
+    dvv = np.zeros(v.shape)
+    for b0 in range(0, L, row_block):
+        rb = np.arange(b0, min(L, b0 + row_block))
+        mask = baseline_mask(n, k, mode, C, W, rows=rb)
+        for h in range(Hq):
+            a, b, c = attention_masked_backward(q[rb, h], kx[:, h // g], v[:, h // g], mask,
+                                                scale, dout[rb, h])
+            dq[rb, h] = a
+            dk[:, h // g] += b
+            dvv[:, h // g] += c
+    return dq, dk, dvv
 
 
 def visible_pairs_bruteforce(n: int, k: int, C: int,
