@@ -154,6 +154,29 @@ KSA_API int32_t ksa_prefill_attn_mode(const ksa_params* p, int32_t mode, int64_t
                               int64_t n_text, const void* q, const void* k, const void* v, void* out,
                               float* lse, void* stream);
 
+/* Bytes of workspace ksa_prefill_attn_bwd needs for this shape (it depends
+ * on the kernel the shape runs on); 0 on bad input. */
+KSA_API size_t ksa_prefill_bwd_workspace_bytes(const ksa_params* p, int32_t batch, int64_t n_text);
+
+/* Backward of ksa_prefill_attn_mode: gradients of the attention output with
+ * respect to q, k and v (the report trains with its block-sparse kernel,
+ * Sec. 2.3; the gradient is the chain rule through Eq. 10 over the same
+ * visible pairs).  Inputs are those of the forward call plus
+ *   out  [batch, L, Hq, Dv]  the forward output
+ *   dout [batch, L, Hq, Dv]  gradient of the loss with respect to out
+ *   lse  [batch, Hq, L] fp32 the forward's natural-log normaliser (required)
+ * and outputs (every element written; dk/dv of a kv head sum its query heads)
+ *   dq [batch, L, Hq, Dqk], dk [batch, L, Hkv, Dqk], dv [batch, L, Hkv, Dv]
+ * in the params' dtype.  workspace (device, >= ksa_prefill_bwd_workspace_bytes)
+ * holds per-row dot(dout, out) and, on the MFMA path, per-segment partial
+ * gradients of the summary keys; its contents on entry do not matter.
+ * v_is_k_prefix (absorbed MLA) is KSA_STATUS_UNSUPPORTED.  Rows that see no
+ * key do not exist under these rules. */
+KSA_API int32_t ksa_prefill_attn_bwd(const ksa_params* p, int32_t mode, int64_t window_tokens, int32_t batch,
+                             int64_t n_text, const void* q, const void* k, const void* v,
+                             const void* out, const void* dout, const float* lse, void* dq, void* dk,
+                             void* dv, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Slots per (sequence, kv head): 1 + k + C*k + max_summaries; -1 on bad input. */
 KSA_API int64_t ksa_cache_slots(const ksa_params* p, int32_t max_summaries);
 

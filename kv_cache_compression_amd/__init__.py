@@ -33,7 +33,8 @@ KSA_CACHE_ERR_BAD_SUMMARY_READ = 8
 # Every symbol the header declares.
 EXPORTS = (
     "ksa_status_string", "ksa_last_error_message", "ksa_augmented_len", "ksa_rope_augmented",
-    "ksa_rope_positions", "ksa_prefill_attn", "ksa_prefill_attn_mode", "ksa_cache_slots", "ksa_cache_reset",
+    "ksa_rope_positions", "ksa_prefill_attn", "ksa_prefill_attn_mode", "ksa_prefill_bwd_workspace_bytes",
+    "ksa_prefill_attn_bwd", "ksa_cache_slots", "ksa_cache_reset",
     "ksa_cache_append", "ksa_cache_fill", "ksa_decode_workspace_bytes", "ksa_decode_attn",
     "ksa_cache_read_errors",
 )
@@ -88,6 +89,8 @@ _SIGS = {
     "ksa_rope_positions": (_i32, [_P, _i64, _vp, _vp, _i32, _i32, _i32, _i32, ctypes.c_double, _vp]),
     "ksa_prefill_attn": (_i32, [_P, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
     "ksa_prefill_attn_mode": (_i32, [_P, _i32, _i64, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "ksa_prefill_bwd_workspace_bytes": (ctypes.c_size_t, [_P, _i32, _i64]),
+    "ksa_prefill_attn_bwd": (_i32, [_P, _i32, _i64, _i32, _i64] + [_vp] * 10 + [ctypes.c_size_t, _vp]),
     "ksa_cache_slots": (_i64, [_P, _i32]),
     "ksa_cache_reset": (_i32, [_P, _C, _i32, _vp]),
     "ksa_cache_append": (_i32, [_P, _C, _i32, _vp, _vp, _vp, _vp]),
@@ -241,6 +244,41 @@ def ksa_prefill_attn_mode(p: Params, mode: int, window_tokens: int, q: torch.Ten
                                        None if p.v_is_k_prefix else _ptr(v), _ptr(out), _ptr(lse),
                                        _stream(stream)))
     return out
+
+
+def ksa_prefill_bwd_workspace_bytes(p: Params, batch: int, n_text: int) -> int:
+    pc = p.c()
+    return int(lib().ksa_prefill_bwd_workspace_bytes(ctypes.byref(pc), batch, n_text))
+
+
+def ksa_prefill_attn_bwd(p: Params, mode: int, window_tokens: int, q: torch.Tensor, k: torch.Tensor,
+                         v: torch.Tensor, out: torch.Tensor, dout: torch.Tensor, lse: torch.Tensor,
+                         n_text: int, dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+                         dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                         stream=None):
+    """Backward of :func:`ksa_prefill_attn_mode`.  ``lse`` is the forward's
+    [B, Hq, L] fp32 normaliser.  Returns (dq, dk, dv)."""
+    B, _ = _prefill_buffers(p, q, k, v, n_text, out, lse)
+    L = ksa_augmented_len(n_text, p.chunk_size)
+    _need(dout, (B, L, p.num_q_heads, p.head_dim_v), p.dtype, "dout")
+    if lse is None:
+        raise ValueError("the backward needs the forward's lse")
+    mk = lambda shape: torch.empty(shape, dtype=p.dtype, device=q.device)
+    dq = mk(q.shape) if dq is None else dq
+    dk = mk(k.shape) if dk is None else dk
+    dv = mk(v.shape) if dv is None else dv
+    _need(dq, tuple(q.shape), p.dtype, "dq")
+    _need(dk, tuple(k.shape), p.dtype, "dk")
+    _need(dv, tuple(v.shape), p.dtype, "dv")
+    need = ksa_prefill_bwd_workspace_bytes(p, B, n_text)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    pc = p.c()
+    _check(lib().ksa_prefill_attn_bwd(ctypes.byref(pc), mode, window_tokens, B, n_text, _ptr(q), _ptr(k),
+                                      _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                                      _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      _stream(stream)))
+    return dq, dk, dv
 
 
 def ksa_cache_slots(p: Params, max_summaries: int) -> int:

@@ -162,19 +162,18 @@ int32_t ksa_rope_positions(const ksa_params* p, int64_t rows, const int64_t* pos
   return rope_common(p, ra, x, stream);
 }
 
-int32_t ksa_prefill_attn_mode(const ksa_params* p, int32_t mode, int64_t window_tokens, int32_t batch,
-                              int64_t n_text, const void* q, const void* k, const void* v, void* out,
-                              float* lse, void* stream) {
-  if (int32_t st = check_params(p)) return st;
+namespace {
+
+int32_t check_mode(int32_t mode, int64_t window_tokens) {
   if (mode != KSA_MODE_KSA && mode != KSA_MODE_SCA && mode != KSA_MODE_SWA)
     return fail(KSA_STATUS_INVALID_ARGUMENT, "unknown prefill mode");
   if (mode == KSA_MODE_SWA && window_tokens < 1)
     return fail(KSA_STATUS_INVALID_ARGUMENT, "token window must be at least 1");
-  if (batch < 0 || n_text < 0) return fail(KSA_STATUS_INVALID_ARGUMENT, "negative batch/n_text");
-  if (n_text > (int64_t(1) << 40)) return fail(KSA_STATUS_UNSUPPORTED, "n_text too large");
-  if (batch == 0 || n_text == 0) return KSA_STATUS_OK;
-  if (!q || !k || !out || (!p->v_is_k_prefix && !v))
-    return fail(KSA_STATUS_INVALID_ARGUMENT, "q/k/v/out pointer is NULL");
+  return KSA_STATUS_OK;
+}
+
+ksa::PrefillArgs prefill_args(const ksa_params* p, int32_t mode, int64_t window_tokens, int32_t batch,
+                              int64_t n_text) {
   ksa::PrefillArgs a;
   a.batch = batch;
   a.n_text = n_text;
@@ -190,11 +189,63 @@ int32_t ksa_prefill_attn_mode(const ksa_params* p, int32_t mode, int64_t window_
   a.mode = mode;
   // a window wider than the sequence is the whole causal prefix
   a.window_tokens = mode == KSA_MODE_SWA ? (window_tokens < n_text ? window_tokens : n_text) : 0;
+  return a;
+}
+
+}  // namespace
+
+int32_t ksa_prefill_attn_mode(const ksa_params* p, int32_t mode, int64_t window_tokens, int32_t batch,
+                              int64_t n_text, const void* q, const void* k, const void* v, void* out,
+                              float* lse, void* stream) {
+  if (int32_t st = check_params(p)) return st;
+  if (int32_t st = check_mode(mode, window_tokens)) return st;
+  if (batch < 0 || n_text < 0) return fail(KSA_STATUS_INVALID_ARGUMENT, "negative batch/n_text");
+  if (n_text > (int64_t(1) << 40)) return fail(KSA_STATUS_UNSUPPORTED, "n_text too large");
+  if (batch == 0 || n_text == 0) return KSA_STATUS_OK;
+  if (!q || !k || !out || (!p->v_is_k_prefix && !v))
+    return fail(KSA_STATUS_INVALID_ARGUMENT, "q/k/v/out pointer is NULL");
+  const ksa::PrefillArgs a = prefill_args(p, mode, window_tokens, batch, n_text);
   g_msg[0] = 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (ksa::prefill_mfma_supported(a, p->dtype))
     return hip_status(ksa::launch_prefill_mfma_d128(a, q, k, v, out, lse, s), "prefill");
   return hip_status(ksa::launch_prefill_generic(a, p->dtype, 0, q, k, v, out, lse, s), "prefill");
+}
+
+static size_t bwd_workspace(const ksa::PrefillArgs& a, int32_t dtype) {
+  const size_t delta = static_cast<size_t>(a.batch) * a.hq * a.L * sizeof(float);
+  return (delta + 255) / 256 * 256;
+}
+
+size_t ksa_prefill_bwd_workspace_bytes(const ksa_params* p, int32_t batch, int64_t n_text) {
+  if (check_params(p) || batch < 0 || n_text < 0 || n_text > (int64_t(1) << 40)) return 0;
+  return bwd_workspace(prefill_args(p, KSA_MODE_KSA, 0, batch, n_text), p->dtype);
+}
+
+int32_t ksa_prefill_attn_bwd(const ksa_params* p, int32_t mode, int64_t window_tokens, int32_t batch,
+                             int64_t n_text, const void* q, const void* k, const void* v, const void* out,
+                             const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  if (int32_t st = check_params(p)) return st;
+  if (int32_t st = check_mode(mode, window_tokens)) return st;
+  if (p->v_is_k_prefix) return fail(KSA_STATUS_UNSUPPORTED, "backward of the absorbed (v_is_k_prefix) form");
+  if (batch < 0 || n_text < 0) return fail(KSA_STATUS_INVALID_ARGUMENT, "negative batch/n_text");
+  if (n_text > (int64_t(1) << 40)) return fail(KSA_STATUS_UNSUPPORTED, "n_text too large");
+  if (batch == 0 || n_text == 0) return KSA_STATUS_OK;
+  if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv)
+    return fail(KSA_STATUS_INVALID_ARGUMENT, "a tensor pointer is NULL");
+  const ksa::PrefillArgs a = prefill_args(p, mode, window_tokens, batch, n_text);
+  const size_t need = bwd_workspace(a, p->dtype);
+  if (!workspace || workspace_bytes < need)
+    return fail(KSA_STATUS_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", need,
+                workspace ? workspace_bytes : size_t(0));
+  g_msg[0] = 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* delta = static_cast<float*>(workspace);
+  if (int32_t st = hip_status(ksa::launch_bwd_delta(a, p->dtype, out, dout, delta, s), "prefill_bwd"))
+    return st;
+  return hip_status(ksa::launch_prefill_bwd_generic(a, p->dtype, q, k, v, dout, lse, delta, dq, dk, dv, s),
+                    "prefill_bwd");
 }
 
 int32_t ksa_prefill_attn(const ksa_params* p, int32_t batch, int64_t n_text, const void* q,

@@ -41,6 +41,14 @@ hipError_t launch_prefill_mfma_d128(const PrefillArgs& a, const void* q, const v
                                     const void* v, void* out, float* lse, hipStream_t s);
 bool prefill_mfma_supported(const PrefillArgs& a, int32_t dtype);
 
+// Backward of the prefill.  delta[b, h, row] = dot(dout, out) in fp32.
+hipError_t launch_bwd_delta(const PrefillArgs& a, int32_t dtype, const void* out, const void* dout,
+                            float* delta, hipStream_t s);
+// Generic dq / dk / dv kernels (wave per row), any dtype and head dims.
+hipError_t launch_prefill_bwd_generic(const PrefillArgs& a, int32_t dtype, const void* q, const void* k,
+                                      const void* v, const void* dout, const float* lse, const float* delta,
+                                      void* dq, void* dk, void* dv, hipStream_t s);
+
 struct CacheArgs {
   int32_t batch, k, C, hkv, dqk, dv;
   int32_t v_is_k_prefix;

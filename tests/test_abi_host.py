@@ -30,7 +30,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(L):
     decl = _declared()
-    assert len(decl) == 14
+    assert len(decl) == 16
     assert sorted(K.EXPORTS) == decl
     for name in decl:
         assert hasattr(L, name), name
@@ -94,6 +94,28 @@ def test_prefill_mode_arguments(L):
     assert rc == 1  # v missing
     for mode in (0, 1, 2):
         assert L.ksa_prefill_attn_mode(ctypes.byref(p), mode, 5, 0, 512, None, None, None, None, None, None) == 0
+
+
+def test_prefill_bwd_arguments(L):
+    p = _params()
+    fake = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    need = L.ksa_prefill_bwd_workspace_bytes(ctypes.byref(p), 2, 512)
+    assert need >= 2 * 4 * 576 * 4
+    assert L.ksa_prefill_bwd_workspace_bytes(None, 2, 512) == 0
+
+    def call(params, mode=0, W=0, ptrs=(fake,) * 9, ws=fake, wsb=need, batch=2):
+        return _status(L, L.ksa_prefill_attn_bwd(ctypes.byref(params), mode, W, batch, 512, *ptrs, ws, wsb, None))
+
+    assert call(p, mode=5)[0] == 1
+    assert call(p, mode=2, W=0)[0] == 1
+    rc, msg = call(p, ptrs=(fake,) * 5 + (None,) + (fake,) * 3)
+    assert rc == 1 and "NULL" in msg  # lse is required
+    rc, msg = call(p, wsb=need - 1)
+    assert rc == 4 and "workspace" in msg
+    assert call(p, ws=None)[0] == 4
+    mla = _params(head_dim_qk=64, head_dim_v=32, v_is_k_prefix=1)
+    assert call(mla)[0] == 2
+    assert call(p, batch=0, ptrs=(None,) * 9, ws=None, wsb=0)[0] == 0
 
 
 def test_cache_argument_checks(L):
