@@ -18,6 +18,7 @@ SOURCES = [
     "ksa_prefill_generic.hip",
     "ksa_prefill_mfma.hip",
     "ksa_prefill_bwd_generic.hip",
+    "ksa_prefill_bwd_mfma.hip",
     "ksa_cache.hip",
     "ksa_decode.hip",
     "ksa_decode_mla.hip",

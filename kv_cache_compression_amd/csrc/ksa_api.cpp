@@ -212,9 +212,14 @@ int32_t ksa_prefill_attn_mode(const ksa_params* p, int32_t mode, int64_t window_
   return hip_status(ksa::launch_prefill_generic(a, p->dtype, 0, q, k, v, out, lse, s), "prefill");
 }
 
+// [delta: batch * Hq * L fp32, 256-byte aligned][MFMA path: summary-key partials]
+static size_t bwd_delta_bytes(const ksa::PrefillArgs& a) {
+  return (static_cast<size_t>(a.batch) * a.hq * a.L * sizeof(float) + 255) / 256 * 256;
+}
 static size_t bwd_workspace(const ksa::PrefillArgs& a, int32_t dtype) {
-  const size_t delta = static_cast<size_t>(a.batch) * a.hq * a.L * sizeof(float);
-  return (delta + 255) / 256 * 256;
+  size_t n = bwd_delta_bytes(a);
+  if (ksa::prefill_bwd_mfma_supported(a, dtype)) n += ksa::prefill_bwd_mfma_partial_bytes(a);
+  return n;
 }
 
 size_t ksa_prefill_bwd_workspace_bytes(const ksa_params* p, int32_t batch, int64_t n_text) {
@@ -244,6 +249,11 @@ int32_t ksa_prefill_attn_bwd(const ksa_params* p, int32_t mode, int64_t window_t
   float* delta = static_cast<float*>(workspace);
   if (int32_t st = hip_status(ksa::launch_bwd_delta(a, p->dtype, out, dout, delta, s), "prefill_bwd"))
     return st;
+  if (ksa::prefill_bwd_mfma_supported(a, p->dtype)) {
+    float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_delta_bytes(a));
+    return hip_status(ksa::launch_prefill_bwd_mfma(a, q, k, v, dout, lse, delta, part, dq, dk, dv, s),
+                      "prefill_bwd");
+  }
   return hip_status(ksa::launch_prefill_bwd_generic(a, p->dtype, q, k, v, dout, lse, delta, dq, dk, dv, s),
                     "prefill_bwd");
 }

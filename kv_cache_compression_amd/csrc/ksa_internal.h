@@ -49,6 +49,14 @@ hipError_t launch_prefill_bwd_generic(const PrefillArgs& a, int32_t dtype, const
                                       const void* v, const void* dout, const float* lse, const float* delta,
                                       void* dq, void* dk, void* dv, hipStream_t s);
 
+// bf16 MFMA backward, Dqk = Dv = 128: dq kernel, dk/dv kernel, summary-key
+// reduce.  part: fp32 partials of the summary keys (prefill_bwd_mfma_partial_bytes).
+bool prefill_bwd_mfma_supported(const PrefillArgs& a, int32_t dtype);
+size_t prefill_bwd_mfma_partial_bytes(const PrefillArgs& a);
+hipError_t launch_prefill_bwd_mfma(const PrefillArgs& a, const void* q, const void* k, const void* v,
+                                   const void* dout, const float* lse, const float* delta, float* part,
+                                   void* dq, void* dk, void* dv, hipStream_t s);
+
 struct CacheArgs {
   int32_t batch, k, C, hkv, dqk, dv;
   int32_t v_is_k_prefix;

@@ -1,0 +1,60 @@
+// Helpers of the bf16 MFMA kernels with 128-wide heads (gfx950, wave64):
+// swizzled LDS row layout, transposing LDS reads, bf16 packing, and the
+// fast floor(t / k) used to map text indices to Eq. 1 rows.
+#pragma once
+
+#include "ksa_common.h"
+
+namespace ksa {
+namespace mfma {
+
+constexpr int D = 128;
+constexpr int ROW_BYTES = D * 2;  // 256 B per (row, head)
+
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+
+// 16-byte chunk c (0..15) of LDS row `row` is stored at chunk c ^ swz(row):
+// 8 consecutive rows hit 8 different even chunks and the next 8 the odd
+// ones, so MFMA operand reads (32 rows x 16 B) and transposing reads
+// (4 rows x 32 B per 16 lanes) spread over the banks.
+__device__ __forceinline__ int lds_swz(int row) { return ((row & 7) << 1) | ((row >> 3) & 1); }
+__device__ __forceinline__ int lds_off(int row, int chunk) {
+  return row * ROW_BYTES + ((chunk ^ lds_swz(row)) << 4);
+}
+
+// ds_read_b64_tr_b16: in each group of 16 lanes, lane 4 rr + c4 names row
+// rr and columns 4 c4 .. 4 c4 + 3 of a 4 x 16 bf16 block; lane i receives
+// column i (4 values, rows 0..3).
+__device__ __forceinline__ bf16x4_t lds_read_tr(const char* base, int byte_off) {
+  auto p = (lds_bf16x4_t*)((__attribute__((address_space(3))) char*)(base) + byte_off);
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p);
+}
+
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+}
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Takes the word by value: __builtin_bit_cast applied directly to a vector
+// element (v.y) reads element 0 with this compiler.
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2_t, w); }
+
+// floor(t / d) = (umulhi(t, m) + t) >> l for 0 <= t < 2^31.
+inline void fast_div(uint32_t d, uint32_t* m, uint32_t* l) {
+  uint32_t s = 0;
+  while ((uint64_t(1) << s) < d) ++s;
+  *l = s;
+  *m = static_cast<uint32_t>(((uint64_t(1) << 32) * ((uint64_t(1) << s) - d)) / d + 1);
+}
+__device__ __forceinline__ int32_t fast_div_apply(int32_t t, uint32_t m, uint32_t l) {
+  return static_cast<int32_t>((__umulhi(static_cast<uint32_t>(t), m) + static_cast<uint32_t>(t)) >> l);
+}
+
+}  // namespace mfma
+}  // namespace ksa

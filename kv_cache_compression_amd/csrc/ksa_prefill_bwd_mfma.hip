@@ -1,0 +1,835 @@
+// Backward of the block-sparse KSA prefill for bf16, Dqk = Dv = 128, on
+// gfx950 MFMA.
+//
+// The forward ("Kwai Summary Attention Technical Report", Sec. 2.3, Eq. 10)
+// is softmax attention over the visible pairs of Eq. (3); the backward
+// recomputes p_ij = exp(scale q_i.k_j - lse_i) from the forward's
+// normaliser and, with delta_i = dout_i . out_i, forms
+// dS_ij = p_ij (dout_i . v_j - delta_i).  Three kernels, no atomics:
+//
+// dq kernel (the forward's tiling: a workgroup owns 128 query rows of one
+// kv head's group, 32 rows per wave, and walks the same two key runs in
+// 64-key tiles):
+//   S^T = K Q^T and dP^T = V dO^T on v_mfma_f32_32x32x16_bf16 (A = K / V
+//   rows from LDS, B = Q / dO held in registers), dS^T in registers, then
+//   dQ^T += K^T dS^T with K^T read through ds_read_b64_tr_b16.  Summary
+//   query rows (k + 1 keys each) run in the first workgroups, one wave per
+//   (sequence, kv head, summary).
+//
+// dkdv kernel (keys fixed, queries streamed): a workgroup owns 128 keys of
+// one kv head, 32 per wave, held in registers as B operands; it walks the
+// query tiles (64 rows of one query head) that see them, for every head of
+// the group:
+//   S = Q K^T and dP = dO V^T (A = Q / dO rows from LDS), P and dS in
+//   registers, dV^T += dO^T P and dK^T += Q^T dS (A = dO^T / Q^T through
+//   transposing LDS reads).
+//   Text keys x (chunk c) are seen by text t_x .. t_{(c+C+1)k-1} (or the
+//   token window) and by the summary s_c: one workgroup covers all of them
+//   and writes dk, dv.  Summary keys s_j are seen by every text t_i with
+//   floor(i/k) >= j + C + 1 (KSA only), a range that grows towards the start
+//   of the sequence; it is cut into segments of equal length, one
+//   workgroup per (128 summaries, segment), each writing fp32 partial sums.
+// reduce kernel: one wave per (sequence, kv head, summary) adds the
+// segments' partials and the summary query's own pair (s_j sees itself)
+// and writes dk, dv of the summary rows.
+#include <type_traits>
+
+#include "ksa_internal.h"
+#include "ksa_mfma_common.h"
+
+namespace ksa {
+
+namespace {
+
+using namespace mfma;
+
+constexpr int BN = 64;                      // keys (dq) or queries (dkdv) per tile
+constexpr int TILE_BYTES = BN * ROW_BYTES;  // 16 KB
+constexpr int KW = 128;                     // keys per dkdv workgroup
+constexpr int SUM_R = 16;                   // key rows per pass of a summary query wave
+
+struct BwdArgs {
+  int32_t batch, n, L, k, C, hq, hkv, g, M;
+  int32_t mode, W;
+  uint32_t divk_m, divk_l;
+  float sl;     // softmax scale * log2(e)
+  float scale;  // softmax scale
+  // dq kernel
+  int32_t n_tiles, n_hg, n_sum_blocks;
+  // dkdv kernel
+  int32_t n_sum_wg;  // summary-key workgroups (all sequences and heads)
+  int32_t nt_sum;    // 128-summary tiles per head
+  int32_t nu, qseg;  // query segments of the summary keys, their length
+  int64_t part_stride_bh;  // floats of partials per (sequence, kv head)
+};
+
+__device__ __forceinline__ int32_t div_k(const BwdArgs& a, int32_t t) {
+  return fast_div_apply(t, a.divk_m, a.divk_l);
+}
+__device__ __forceinline__ int32_t trow(const BwdArgs& a, int32_t t) { return t + div_k(a, t); }
+
+// Number of 128-summary tiles whose first visible text query lies in
+// segment u or before it (and before n): the tiles with a workgroup for u.
+__device__ __forceinline__ int32_t seg_tiles(const BwdArgs& a, int32_t u) {
+  const int32_t lim = min(a.n, (u + 1) * a.qseg) - 1;  // last query of the segment
+  const int32_t top = div_k(a, lim) - a.C - 1;         // largest summary it sees
+  if (top < 0) return 0;
+  return min(a.nt_sum, top / KW + 1);
+}
+
+// ---------------------------------------------------------------------------
+// Summary query rows: dq of s_j over its k + 1 keys.  Lane (hh, c) holds
+// dims 8c .. 8c+7 of head hh of a group of four.
+// ---------------------------------------------------------------------------
+__device__ void summary_dq_wave(const BwdArgs& a, int64_t item, const bf16_t* __restrict__ q,
+                                const bf16_t* __restrict__ kx, const bf16_t* __restrict__ vx,
+                                const bf16_t* __restrict__ dout, const float* __restrict__ lse,
+                                const float* __restrict__ delta, bf16_t* __restrict__ dq) {
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 15;
+  const int hh = lane >> 4;
+  const int j = static_cast<int>(item % a.M);
+  const int kvh = static_cast<int>((item / a.M) % a.hkv);
+  const int b = static_cast<int>(item / (static_cast<int64_t>(a.M) * a.hkv));
+  const int r0 = j * (a.k + 1);
+  const int nrows = a.k + 1;
+  const int srow = r0 + a.k;
+  const int64_t kvs = static_cast<int64_t>(a.hkv) * D;
+  const bf16_t* kb = kx + static_cast<int64_t>(b) * a.L * kvs + kvh * D + 8 * c;
+  const bf16_t* vb = vx + static_cast<int64_t>(b) * a.L * kvs + kvh * D + 8 * c;
+  for (int hg = 0; hg < a.g; hg += 4) {
+    const int hloc = hg + hh;
+    const bool hval = hloc < a.g;
+    const int h = kvh * a.g + (hval ? hloc : 0);
+    const int64_t qo = (static_cast<int64_t>(b) * a.L + srow) * a.hq * D + static_cast<int64_t>(h) * D + 8 * c;
+    const u32x4_t qw = *reinterpret_cast<const u32x4_t*>(q + qo);
+    const u32x4_t gw = *reinterpret_cast<const u32x4_t*>(dout + qo);
+    const int64_t so = (static_cast<int64_t>(b) * a.hq + h) * a.L + srow;
+    const float lse2 = lse[so] * kLog2e;
+    const float dl = delta[so];
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < nrows; s0 += SUM_R) {
+      u32x4_t kw[SUM_R], vw[SUM_R];
+#pragma unroll
+      for (int r = 0; r < SUM_R; ++r) {
+        const int row = r0 + min(s0 + r, nrows - 1);
+        kw[r] = *reinterpret_cast<const u32x4_t*>(kb + row * kvs);
+        vw[r] = *reinterpret_cast<const u32x4_t*>(vb + row * kvs);
+      }
+#pragma unroll
+      for (int r = 0; r < SUM_R; ++r) {
+        float s = 0.f, dp = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qw[e]), as_bf16x2(kw[r][e]), s, false);
+          dp = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(gw[e]), as_bf16x2(vw[r][e]), dp, false);
+        }
+#pragma unroll
+        for (int o = 8; o >= 1; o >>= 1) {
+          s += __shfl_xor(s, o);
+          dp += __shfl_xor(dp, o);
+        }
+        const float p = fast_exp2(fmaf(s, a.sl, -lse2));
+        const float ds = s0 + r < nrows ? p * (dp - dl) : 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += ds * bf_lo(kw[r][e]);
+          acc[2 * e + 1] += ds * bf_hi(kw[r][e]);
+        }
+      }
+    }
+    if (hval) {
+      u32x4_t w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = pk_bf16(acc[2 * e] * a.scale, acc[2 * e + 1] * a.scale);
+      *reinterpret_cast<u32x4_t*>(dq + qo) = w;
+    }
+  }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// dq of the text query rows.
+// ---------------------------------------------------------------------------
+template <int HPW>
+__global__ void __launch_bounds__(256, 2) bwd_dq_d128_kernel(
+    BwdArgs a, const bf16_t* __restrict__ q, const bf16_t* __restrict__ kx, const bf16_t* __restrict__ vx,
+    const bf16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
+    bf16_t* __restrict__ dq) {
+  constexpr int PT = 32 * (4 / HPW);  // text positions per workgroup
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (static_cast<int>(blockIdx.x) < a.n_sum_blocks) {
+    const int64_t item = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+    if (item < static_cast<int64_t>(a.batch) * a.hkv * a.M)
+      summary_dq_wave(a, item, q, kx, vx, dout, lse, delta, dq);
+    return;
+  }
+  const int n_slots = a.batch * a.hkv * a.n_hg;
+  const int bid = blockIdx.x - a.n_sum_blocks;
+  const int hslot = bid % n_slots;
+  const int tile = a.n_tiles - 1 - bid / n_slots;  // longest first
+  const int hg = hslot % a.n_hg;
+  const int kvh = (hslot / a.n_hg) % a.hkv;
+  const int b = hslot / (a.n_hg * a.hkv);
+  const int h = kvh * a.g + hg * HPW + (wave % HPW);
+
+  // Key runs of the workgroup (as in the forward).
+  const int p0 = tile * PT;
+  const int p_last = (p0 + PT < a.n ? p0 + PT : a.n) - 1;
+  const int c_first = div_k(a, p0), c_last = div_k(a, p_last);
+  const int sn = a.mode == KSA_MODE_KSA && c_last - a.C > 0 ? c_last - a.C : 0;
+  const int t0 = a.mode == KSA_MODE_SWA ? (p0 - a.W + 1 > 0 ? p0 - a.W + 1 : 0)
+                                        : (c_first - a.C > 0 ? (c_first - a.C) * a.k : 0);
+  const int ns = (sn + BN - 1) / BN;
+  const int n_total = ns + (p_last - t0 + BN) / BN;
+
+  const int iw0 = p0 + 32 * (wave / HPW);
+  const int iw1 = iw0 + 31 < a.n ? iw0 + 31 : a.n - 1;
+  const bool wave_active = iw0 < a.n;
+  const int qi = iw0 + (lane & 31);
+  const bool q_valid = qi < a.n;
+  const int ci = div_k(a, q_valid ? qi : 0);
+  const int smax = q_valid ? ci - a.C - 1 : -1;
+  auto text_lo = [&](int i, int c) {
+    return a.mode == KSA_MODE_SWA ? (i - a.W + 1 > 0 ? i - a.W + 1 : 0) : (c - a.C > 0 ? (c - a.C) * a.k : 0);
+  };
+  const int tlo = q_valid ? text_lo(qi, ci) : 0x7fffffff;
+  const int cw0 = div_k(a, wave_active ? iw0 : 0), cw1 = div_k(a, wave_active ? iw1 : 0);
+  const int tlo_w1 = text_lo(wave_active ? iw1 : 0, cw1);
+
+  // Q^T and dO^T as B operands: column = query (lane % 32), k-slots
+  // d = 16 ks + 8 (lane / 32) + j.
+  const int half = lane >> 5;
+  const int qrow = trow(a, q_valid ? qi : 0);
+  bf16x8_t qop[8], gop[8];
+  {
+    const int64_t o = (static_cast<int64_t>(b) * a.L + qrow) * a.hq * D + static_cast<int64_t>(h) * D + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      qop[ks] = q_valid ? *reinterpret_cast<const bf16x8_t*>(q + o + 16 * ks) : bf16x8_t{};
+      gop[ks] = q_valid ? *reinterpret_cast<const bf16x8_t*>(dout + o + 16 * ks) : bf16x8_t{};
+    }
+  }
+  const int64_t so = (static_cast<int64_t>(b) * a.hq + h) * a.L + qrow;
+  const float nlse2 = q_valid ? -lse[so] * kLog2e : 0.f;
+  const float dl = q_valid ? delta[so] : 0.f;
+
+  const int ld_chunk = tid & 15;
+  const int ld_row = tid >> 4;
+  const int kvs = a.hkv * D;
+  const int RB = kvs * 2;
+  const int64_t kv_base = static_cast<int64_t>(b) * a.L * kvs + kvh * D;
+  const int kv_bytes = (a.L * kvs - kvh * D) * 2;
+  const __amdgpu_buffer_rsrc_t rsrc_k = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(kx + kv_base), static_cast<short>(0), kv_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsrc_v = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(vx + kv_base), static_cast<short>(0), kv_bytes, 0x00020000);
+  const int chunk16 = 16 * (ld_chunk ^ lds_swz(ld_row));
+  const int sum_step = (a.k + 1) * RB;
+  const int s_c0 = ld_row * sum_step + a.k * RB + chunk16;
+  const int s_lim = (sn > 0 ? (sn - 1) * sum_step + a.k * RB : 0) + chunk16;
+  __shared__ __attribute__((aligned(16))) char lds_k0[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char lds_k1[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char lds_v0[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char lds_v1[TILE_BYTES];
+  char* const lds_k[2] = {lds_k0, lds_k1};
+  char* const lds_v[2] = {lds_v0, lds_v1};
+  auto load_tile = [&](const __amdgpu_buffer_rsrc_t& rs, char* buf, int tt) {
+    int vo[4];
+    if (tt < ns) {
+      const int sb = s_c0 + tt * BN * sum_step;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) vo[u] = min(sb + 16 * u * sum_step, s_lim);
+    } else {
+      const int x0 = t0 + (tt - ns) * BN + ld_row;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int x = min(x0 + 16 * u, p_last);
+        vo[u] = static_cast<int>(__umul24(static_cast<uint32_t>(trow(a, x)), RB)) + chunk16;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(buf + (64 * wave + 256 * u) * 16), 16, vo[u], 0, 0, 0);
+  };
+
+  // Row-operand offsets (K / V rows lane % 32 (+32), chunk 2 ks + half) and
+  // transposing offsets of K^T: in 16-lane group G, lane (4 rr + c4) points
+  // at key row 16 ks + 8 rd + 4 (G / 2) + rr and d = 32 db + 16 (G % 2) + 4 c4.
+  int koff0, toff[2][4];
+  {
+    const int G = lane >> 4, l16 = lane & 15, rr = l16 >> 2, c4 = l16 & 3;
+    koff0 = lds_off(lane & 31, half);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int d = 32 * db + 16 * (G & 1) + 4 * c4;
+      const int row0 = 4 * (G >> 1) + rr;
+      toff[0][db] = lds_off(row0, d >> 3) + 2 * (d & 7);
+      toff[1][db] = lds_off(row0 + 8, d >> 3) + 2 * (d & 7);
+    }
+  }
+
+  f32x16_t dqacc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dqacc[db][r] = 0.f;
+
+  auto iter = [&](auto cur_c, int tt) __attribute__((always_inline)) {
+    constexpr int cur = decltype(cur_c)::value;
+    if (tt + 1 < n_total) {
+      load_tile(rsrc_k, lds_k[cur ^ 1], tt + 1);
+      load_tile(rsrc_v, lds_v[cur ^ 1], tt + 1);
+    }
+    const char* kl = lds_k[cur];
+    const char* vl = lds_v[cur];
+    f32x16_t s[2], dp[2];
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb2][r] = dp[kb2][r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        const int off = (koff0 ^ (ks << 5)) + 32 * ROW_BYTES * kb2;
+        const bf16x8_t kop = *reinterpret_cast<const bf16x8_t*>(kl + off);
+        const bf16x8_t vop = *reinterpret_cast<const bf16x8_t*>(vl + off);
+        s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[ks], s[kb2], 0, 0, 0);
+        dp[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, gop[ks], dp[kb2], 0, 0, 0);
+      }
+    // edge tiles: key of (kb2, r) = key0 + 32 kb2 + 8 (r / 4) + 4 half + r % 4
+    const bool is_sum = tt < ns;
+    const int key0 = is_sum ? tt * BN : t0 + (tt - ns) * BN;
+    const bool full = is_sum ? key0 + BN - 1 <= cw0 - a.C - 1 : (key0 >= tlo_w1 && key0 + BN - 1 <= iw0);
+    if (!full) {
+      const int lo = is_sum ? -1 : tlo;
+      const int hi = is_sum ? smax : qi;
+      const int kbase = key0 + 4 * half;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kbase + 32 * kb2 + 8 * (r >> 2) + (r & 3);
+          s[kb2][r] = (key >= lo && key <= hi) ? s[kb2][r] : kNegInf;
+        }
+    }
+    // dS^T packed as the B operand of dQ^T += K^T dS^T (keys 16 ks + ...)
+    u32x4_t pw[4];
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = fast_exp2(fmaf(s[kb2][r], a.sl, nlse2));
+        const float p1 = fast_exp2(fmaf(s[kb2][r + 1], a.sl, nlse2));
+        pw[2 * kb2 + (r >> 3)][(r & 7) >> 1] = pk_bf16(p0 * (dp[kb2][r] - dl), p1 * (dp[kb2][r + 1] - dl));
+      }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, pw[ks]);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const bf16x4_t lo = lds_read_tr(kl, toff[0][db] + 16 * ROW_BYTES * ks);
+        const bf16x4_t hi = lds_read_tr(kl, toff[1][db] + 16 * ROW_BYTES * ks);
+        const bf16x8_t aop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bop, dqacc[db], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  };
+
+  if (n_total > 0) {
+    load_tile(rsrc_k, lds_k[0], 0);
+    load_tile(rsrc_v, lds_v[0], 0);
+    __syncthreads();
+  }
+  for (int tt = 0; tt < n_total; tt += 2) {
+    iter(std::integral_constant<int, 0>(), tt);
+    if (tt + 1 < n_total) iter(std::integral_constant<int, 1>(), tt + 1);
+  }
+  if (!q_valid) return;
+  bf16_t* op = dq + (static_cast<int64_t>(b) * a.L + qrow) * a.hq * D + static_cast<int64_t>(h) * D;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const int d = 32 * db + 8 * qq + 4 * half;
+      uint2 w;
+      w.x = pk_bf16(dqacc[db][4 * qq + 0] * a.scale, dqacc[db][4 * qq + 1] * a.scale);
+      w.y = pk_bf16(dqacc[db][4 * qq + 2] * a.scale, dqacc[db][4 * qq + 3] * a.scale);
+      *reinterpret_cast<uint2*>(op + d) = w;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dk, dv: keys fixed per workgroup, query tiles streamed.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256, 1) bwd_dkdv_d128_kernel(
+    BwdArgs a, const bf16_t* __restrict__ q, const bf16_t* __restrict__ kx, const bf16_t* __restrict__ vx,
+    const bf16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
+    bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, float* __restrict__ part) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int half = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nbh = a.batch * a.hkv;
+  const int bid = blockIdx.x;
+  const bool sum_keys = bid < a.n_sum_wg;
+  int b, kvh, key0, u = 0, nkeys;
+  // query runs: text positions [qt0, qt1) in 64-row tiles, then (text keys
+  // only) summaries [cs0, cs1]
+  int qt0, qt1, cs0 = 0, cs1 = -1;
+  if (sum_keys) {
+    const int slot = bid % nbh;
+    int idx = bid / nbh;
+    b = slot / a.hkv;
+    kvh = slot % a.hkv;
+    int jt = 0;
+    for (u = 0; u < a.nu; ++u) {
+      const int cnt = seg_tiles(a, u);
+      if (idx < cnt) {
+        jt = idx;
+        break;
+      }
+      idx -= cnt;
+    }
+    key0 = jt * KW;
+    nkeys = min(KW, a.M - key0);
+    const int qa = (key0 + a.C + 1) * a.k;  // first text query that sees key0
+    qt0 = max(qa, u * a.qseg) & ~(BN - 1);
+    qt1 = min(a.n, (u + 1) * a.qseg);
+  } else {
+    const int t = bid - a.n_sum_wg;
+    const int slot = t % nbh;
+    b = slot / a.hkv;
+    kvh = slot % a.hkv;
+    key0 = (t / nbh) * KW;
+    nkeys = min(KW, a.n - key0);
+    const int xl = key0 + nkeys - 1;
+    const int hi = a.mode == KSA_MODE_SWA ? xl + a.W - 1 : (div_k(a, xl) + a.C + 1) * a.k - 1;
+    qt0 = key0;
+    qt1 = min(a.n, hi + 1);
+    cs0 = div_k(a, key0);
+    cs1 = min(a.M - 1, div_k(a, xl));
+  }
+  const int ntq = (qt1 - qt0 + BN - 1) / BN;
+  const int nts = cs1 >= cs0 ? (cs1 - cs0 + BN) / BN : 0;
+  const int per_head = ntq + nts;
+  const int n_total = per_head * a.g;
+
+  // This wave's 32 keys; the lane's key is column lane % 32.
+  const int kw0 = key0 + 32 * wave;
+  const int key = kw0 + (lane & 31);
+  const bool key_valid = key < key0 + nkeys;
+  const int krow = sum_keys ? summary_row(key_valid ? key : key0, a.k) : trow(a, key_valid ? key : key0);
+  bf16x8_t kop[8], vop[8];
+  {
+    const int64_t o = (static_cast<int64_t>(b) * a.L + krow) * a.hkv * D + static_cast<int64_t>(kvh) * D + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      kop[ks] = *reinterpret_cast<const bf16x8_t*>(kx + o + 16 * ks);
+      vop[ks] = *reinterpret_cast<const bf16x8_t*>(vx + o + 16 * ks);
+    }
+  }
+  // visibility bounds of the lane's key (text keys): queries [key, khi]
+  const int kc = sum_keys ? 0 : div_k(a, key_valid ? key : key0);
+  const int khi = !key_valid ? -1
+                  : sum_keys ? a.n - 1
+                  : a.mode == KSA_MODE_SWA ? key + a.W - 1
+                                           : (kc + a.C + 1) * a.k - 1;
+  // wave-uniform: the smallest key's upper bound, the largest key
+  const int kwl = min(kw0 + 31, key0 + nkeys - 1);
+  const int whi_min = sum_keys ? 0 : a.mode == KSA_MODE_SWA ? kw0 + a.W - 1 : (div_k(a, kw0) + a.C + 1) * a.k - 1;
+
+  // Q / dO tiles: 64 rows of one query head, rows gathered by the Eq. 1 map.
+  const int qhs = a.hq * D;  // elements per augmented row
+  const int QRB = qhs * 2;
+  const int ld_chunk = tid & 15;
+  const int ld_row = tid >> 4;
+  const int chunk16 = 16 * (ld_chunk ^ lds_swz(ld_row));
+  __shared__ __attribute__((aligned(16))) char lds_q0[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char lds_q1[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char lds_g0[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char lds_g1[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) float lds_st[2][2][BN];  // [buffer][lse2, delta][row]
+  char* const lds_q[2] = {lds_q0, lds_q1};
+  char* const lds_g[2] = {lds_g0, lds_g1};
+  const int64_t qbase = static_cast<int64_t>(b) * a.L * qhs;
+  // iteration it -> (head, kind, first query index of the tile)
+  auto tile_of = [&](int it, int* h, bool* sq, int* i0) {
+    const int hh = it / per_head;
+    const int r = it - hh * per_head;
+    *h = kvh * a.g + hh;
+    *sq = r >= ntq;
+    *i0 = *sq ? cs0 + (r - ntq) * BN : qt0 + r * BN;
+  };
+  auto row_of = [&](bool sq, int idx) { return sq ? summary_row(idx, a.k) : trow(a, idx); };
+  auto load_tile = [&](char* qb, char* gb, int it, float* st_regs) {
+    int h, i0;
+    bool sq;
+    tile_of(it, &h, &sq, &i0);
+    const int last = sq ? cs1 : qt1 - 1;
+    const int hoff = h * D;
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<bf16_t*>(q + qbase + hoff), static_cast<short>(0), (a.L * qhs - hoff) * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<bf16_t*>(dout + qbase + hoff), static_cast<short>(0), (a.L * qhs - hoff) * 2, 0x00020000);
+#pragma unroll
+    for (int uu = 0; uu < 4; ++uu) {
+      const int idx = min(i0 + ld_row + 16 * uu, last);
+      const int vo = static_cast<int>(__umul24(static_cast<uint32_t>(row_of(sq, idx)), QRB)) + chunk16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rq, (__attribute__((address_space(3))) void*)(qb + (64 * wave + 256 * uu) * 16), 16, vo, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rg, (__attribute__((address_space(3))) void*)(gb + (64 * wave + 256 * uu) * 16), 16, vo, 0, 0, 0);
+    }
+    // statistics of the 64 rows: threads 0..63 lse, 64..127 delta
+    if (tid < 2 * BN) {
+      const int rr = tid & (BN - 1);
+      const int idx = min(i0 + rr, last);
+      const int64_t so = (static_cast<int64_t>(b) * a.hq + h) * a.L + row_of(sq, idx);
+      *st_regs = tid < BN ? lse[so] * kLog2e : delta[so];
+    }
+  };
+
+  // LDS offsets: row operands (row lane % 32 (+32), chunk 2 ks + half);
+  // transposing reads (query rows 16 ks + 8 rd + 4 (G / 2) + rr).
+  int qoff0, toff[2][4];
+  {
+    const int G = lane >> 4, l16 = lane & 15, rr = l16 >> 2, c4 = l16 & 3;
+    qoff0 = lds_off(lane & 31, half);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int d = 32 * db + 16 * (G & 1) + 4 * c4;
+      const int row0 = 4 * (G >> 1) + rr;
+      toff[0][db] = lds_off(row0, d >> 3) + 2 * (d & 7);
+      toff[1][db] = lds_off(row0 + 8, d >> 3) + 2 * (d & 7);
+    }
+  }
+
+  f32x16_t dkacc[4], dvacc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dkacc[db][r] = dvacc[db][r] = 0.f;
+
+  auto iter = [&](auto cur_c, int it) __attribute__((always_inline)) {
+    constexpr int cur = decltype(cur_c)::value;
+    float st_next = 0.f;
+    if (it + 1 < n_total) load_tile(lds_q[cur ^ 1], lds_g[cur ^ 1], it + 1, &st_next);
+    int h, i0;
+    bool sq;
+    tile_of(it, &h, &sq, &i0);
+    (void)h;
+    const char* ql = lds_q[cur];
+    const char* gl = lds_g[cur];
+    f32x16_t s[2], dp[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[blk][r] = dp[blk][r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        const int off = (qoff0 ^ (ks << 5)) + 32 * ROW_BYTES * blk;
+        const bf16x8_t qa_ = *reinterpret_cast<const bf16x8_t*>(ql + off);
+        const bf16x8_t ga_ = *reinterpret_cast<const bf16x8_t*>(gl + off);
+        s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa_, kop[ks], s[blk], 0, 0, 0);
+        dp[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga_, vop[ks], dp[blk], 0, 0, 0);
+      }
+    // visibility of (query row 32 blk + 8 (r / 4) + 4 half + r % 4, lane's key)
+    // full: every row of the tile is a query of the run and sees every key
+    // of the wave (the first row the largest key, the last row the smallest)
+    bool full;
+    if (sq)
+      full = false;
+    else if (sum_keys)
+      full = i0 + BN - 1 < qt1 && kwl <= div_k(a, i0) - a.C - 1;
+    else
+      full = i0 + BN - 1 < qt1 && i0 >= kwl && i0 + BN - 1 <= whi_min;
+    if (!full) {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qi = i0 + 32 * blk + 8 * (r >> 2) + 4 * half + (r & 3);
+          bool vis;
+          if (sq)
+            vis = qi <= cs1 && div_k(a, key) == qi && key_valid;
+          else if (sum_keys)
+            vis = qi < qt1 && key <= div_k(a, qi) - a.C - 1 && key_valid;
+          else
+            vis = qi < qt1 && qi >= key && qi <= khi;
+          s[blk][r] = vis ? s[blk][r] : kNegInf;
+        }
+    }
+    const float* st = &lds_st[cur][0][0];
+    u32x4_t pw[4], dw[4];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int row = 32 * blk + 8 * r4 + 4 * half;
+        const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(st + row);
+        const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(st + BN + row);
+        float p[4], ds[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          p[e] = fast_exp2(s[blk][4 * r4 + e] * a.sl - l4[e]);
+          ds[e] = p[e] * (dp[blk][4 * r4 + e] - d4[e]);
+        }
+        // query k-slots of step ks = 2 blk + r4 / 2: rows 16 ks + 4 half + {0..3}, +8
+        const int ks = 2 * blk + (r4 >> 1);
+        const int w0 = 2 * (r4 & 1);
+        pw[ks][w0] = pk_bf16(p[0], p[1]);
+        pw[ks][w0 + 1] = pk_bf16(p[2], p[3]);
+        dw[ks][w0] = pk_bf16(ds[0], ds[1]);
+        dw[ks][w0 + 1] = pk_bf16(ds[2], ds[3]);
+      }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, pw[ks]);
+      const bf16x8_t dop = __builtin_bit_cast(bf16x8_t, dw[ks]);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const bf16x4_t glo = lds_read_tr(gl, toff[0][db] + 16 * ROW_BYTES * ks);
+        const bf16x4_t ghi = lds_read_tr(gl, toff[1][db] + 16 * ROW_BYTES * ks);
+        dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_shufflevector(glo, ghi, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                            pop, dvacc[db], 0, 0, 0);
+        const bf16x4_t qlo = lds_read_tr(ql, toff[0][db] + 16 * ROW_BYTES * ks);
+        const bf16x4_t qhi = lds_read_tr(ql, toff[1][db] + 16 * ROW_BYTES * ks);
+        dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                            dop, dkacc[db], 0, 0, 0);
+      }
+    }
+    if (it + 1 < n_total && tid < 2 * BN) lds_st[cur ^ 1][tid >> 6][tid & (BN - 1)] = st_next;
+    __syncthreads();
+  };
+
+  if (n_total > 0) {
+    float st0 = 0.f;
+    load_tile(lds_q[0], lds_g[0], 0, &st0);
+    if (tid < 2 * BN) lds_st[0][tid >> 6][tid & (BN - 1)] = st0;
+    __syncthreads();
+  }
+  for (int it = 0; it < n_total; it += 2) {
+    iter(std::integral_constant<int, 0>(), it);
+    if (it + 1 < n_total) iter(std::integral_constant<int, 1>(), it + 1);
+  }
+  if (!key_valid) return;
+  // dV^T / dK^T: lane's key column, d = 32 db + 8 qq + 4 half + e
+  if (sum_keys) {
+    float* pp = part + (static_cast<int64_t>(b) * a.hkv + kvh) * a.part_stride_bh +
+                (static_cast<int64_t>(u) * a.nt_sum * KW + key) * 256;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int d = 32 * db + 8 * qq + 4 * half;
+        f32x4_t wk, wv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          wk[e] = dkacc[db][4 * qq + e] * a.scale;
+          wv[e] = dvacc[db][4 * qq + e];
+        }
+        *reinterpret_cast<f32x4_t*>(pp + d) = wk;
+        *reinterpret_cast<f32x4_t*>(pp + 128 + d) = wv;
+      }
+  } else {
+    const int64_t o = (static_cast<int64_t>(b) * a.L + krow) * a.hkv * D + static_cast<int64_t>(kvh) * D;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int d = 32 * db + 8 * qq + 4 * half;
+        uint2 wk, wv;
+        wk.x = pk_bf16(dkacc[db][4 * qq + 0] * a.scale, dkacc[db][4 * qq + 1] * a.scale);
+        wk.y = pk_bf16(dkacc[db][4 * qq + 2] * a.scale, dkacc[db][4 * qq + 3] * a.scale);
+        wv.x = pk_bf16(dvacc[db][4 * qq + 0], dvacc[db][4 * qq + 1]);
+        wv.y = pk_bf16(dvacc[db][4 * qq + 2], dvacc[db][4 * qq + 3]);
+        *reinterpret_cast<uint2*>(dk + o + d) = wk;
+        *reinterpret_cast<uint2*>(dv + o + d) = wv;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Summary keys: partials of the segments plus the summary's own query.
+// One wave per (sequence, kv head, summary); lanes 0..31 own dk dims
+// 4 l .. 4 l + 3, lanes 32..63 own dv dims 4 (l - 32) ...
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) bwd_sum_keys_kernel(BwdArgs a, const bf16_t* __restrict__ q,
+                                                           const bf16_t* __restrict__ kx,
+                                                           const bf16_t* __restrict__ vx,
+                                                           const bf16_t* __restrict__ dout,
+                                                           const float* __restrict__ lse,
+                                                           const float* __restrict__ delta,
+                                                           const float* __restrict__ part,
+                                                           bf16_t* __restrict__ dk, bf16_t* __restrict__ dv) {
+  const int lane = threadIdx.x & 63;
+  const int64_t item = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (item >= static_cast<int64_t>(a.batch) * a.hkv * a.M) return;
+  const int j = static_cast<int>(item % a.M);
+  const int kvh = static_cast<int>((item / a.M) % a.hkv);
+  const int b = static_cast<int>(item / (static_cast<int64_t>(a.M) * a.hkv));
+  const bool is_v = lane >= 32;
+  const int d0 = 4 * (lane & 31);
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  if (a.mode == KSA_MODE_KSA) {
+    const int qa = ((j / KW) * KW + a.C + 1) * a.k;  // first query of the tile's workgroups
+    if (qa < a.n) {
+      const float* pp = part + (static_cast<int64_t>(b) * a.hkv + kvh) * a.part_stride_bh +
+                        static_cast<int64_t>(j) * 256 + (is_v ? 128 : 0) + d0;
+      for (int u = qa / a.qseg; u < a.nu; ++u) {
+        const f32x4_t w = *reinterpret_cast<const f32x4_t*>(pp + static_cast<int64_t>(u) * a.nt_sum * KW * 256);
+        acc += w;
+      }
+    }
+  }
+  // the summary query s_j sees its own key
+  const int srow = summary_row(j, a.k);
+  const int64_t kvo = (static_cast<int64_t>(b) * a.L + srow) * a.hkv * D + static_cast<int64_t>(kvh) * D + d0;
+  const uint2 kw = *reinterpret_cast<const uint2*>(kx + kvo);
+  const uint2 vw = *reinterpret_cast<const uint2*>(vx + kvo);
+  for (int hh = 0; hh < a.g; ++hh) {
+    const int h = kvh * a.g + hh;
+    const int64_t qo = (static_cast<int64_t>(b) * a.L + srow) * a.hq * D + static_cast<int64_t>(h) * D + d0;
+    const uint2 qw = *reinterpret_cast<const uint2*>(q + qo);
+    const uint2 gw = *reinterpret_cast<const uint2*>(dout + qo);
+    // lanes 0..31: q . k; lanes 32..63: dout . v (each over all 128 dims)
+    const uint2 xa = is_v ? gw : qw, xb = is_v ? vw : kw;
+    float part_dot = bf_lo(xa.x) * bf_lo(xb.x) + bf_hi(xa.x) * bf_hi(xb.x) + bf_lo(xa.y) * bf_lo(xb.y) +
+                     bf_hi(xa.y) * bf_hi(xb.y);
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) part_dot += __shfl_xor(part_dot, o);
+    const float other = __shfl_xor(part_dot, 32);
+    const float s = is_v ? other : part_dot;
+    const float dpv = is_v ? part_dot : other;
+    const int64_t so = (static_cast<int64_t>(b) * a.hq + h) * a.L + srow;
+    const float p = fast_exp2(s * a.sl - lse[so] * kLog2e);
+    const float ds = p * (dpv - delta[so]);
+    const float f = is_v ? p : ds * a.scale;
+    const uint2 src = is_v ? gw : qw;
+    acc[0] += f * bf_lo(src.x);
+    acc[1] += f * bf_hi(src.x);
+    acc[2] += f * bf_lo(src.y);
+    acc[3] += f * bf_hi(src.y);
+  }
+  uint2 w;
+  w.x = pk_bf16(acc[0], acc[1]);
+  w.y = pk_bf16(acc[2], acc[3]);
+  *reinterpret_cast<uint2*>((is_v ? dv : dk) + kvo) = w;
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+namespace {
+
+BwdArgs make_args(const PrefillArgs& p) {
+  BwdArgs a{};
+  a.batch = p.batch;
+  a.n = static_cast<int32_t>(p.n_text);
+  a.L = static_cast<int32_t>(p.L);
+  a.k = p.k;
+  a.C = p.C;
+  a.hq = p.hq;
+  a.hkv = p.hkv;
+  a.g = p.hq / p.hkv;
+  a.M = static_cast<int32_t>(p.n_text / p.k);
+  a.mode = p.mode;
+  a.W = static_cast<int32_t>(p.window_tokens);
+  fast_div(static_cast<uint32_t>(a.k), &a.divk_m, &a.divk_l);
+  a.sl = p.scale * kLog2e;
+  a.scale = p.scale;
+  a.nt_sum = (a.M + KW - 1) / KW;
+  // segments of at least 2048 queries, at most 16 per sequence
+  const int64_t seg = ((p.n_text + 15) / 16 + BN - 1) / BN * BN;
+  a.qseg = static_cast<int32_t>(seg > 2048 ? seg : 2048);
+  a.nu = static_cast<int32_t>((p.n_text + a.qseg - 1) / a.qseg);
+  a.part_stride_bh = static_cast<int64_t>(a.nu) * a.nt_sum * KW * 256;
+  return a;
+}
+
+// Host twin of seg_tiles.
+int32_t seg_tiles_host(const BwdArgs& a, int32_t u) {
+  const int32_t lim = std::min(a.n, (u + 1) * a.qseg) - 1;
+  const int32_t top = lim / a.k - a.C - 1;
+  if (top < 0) return 0;
+  return std::min(a.nt_sum, top / KW + 1);
+}
+
+}  // namespace
+
+bool prefill_bwd_mfma_supported(const PrefillArgs& a, int32_t dtype) {
+  const int g = a.hq / a.hkv;
+  // 32-bit byte offsets inside the kernels
+  const bool fits = a.L < (int64_t(1) << 24) && a.L * a.hkv * D * 2 < (int64_t(1) << 31) &&
+                    a.L * static_cast<int64_t>(a.hq) * D * 2 < (int64_t(1) << 31) &&
+                    static_cast<int64_t>(a.batch) * a.hkv * g * ((a.n_text + 31) / 32) < (int64_t(1) << 31);
+  return dtype == KSA_DTYPE_BF16 && a.dqk == D && a.dv == D && !a.v_is_k_prefix && fits &&
+         (g == 1 || g == 2 || g % 4 == 0);
+}
+
+size_t prefill_bwd_mfma_partial_bytes(const PrefillArgs& p) {
+  const BwdArgs a = make_args(p);
+  if (p.mode != KSA_MODE_KSA) return 0;
+  return static_cast<size_t>(a.batch) * a.hkv * a.part_stride_bh * sizeof(float);
+}
+
+template <int HPW>
+static hipError_t launch_dq(BwdArgs a, const void* q, const void* k, const void* v, const void* dout,
+                            const float* lse, const float* delta, void* dq, hipStream_t s) {
+  constexpr int PT = 32 * (4 / HPW);
+  a.n_hg = a.g / HPW;
+  a.n_tiles = (a.n + PT - 1) / PT;
+  const int64_t n_slots = static_cast<int64_t>(a.batch) * a.hkv * a.n_hg;
+  const int64_t sum_items = static_cast<int64_t>(a.batch) * a.hkv * a.M;
+  a.n_sum_blocks = static_cast<int32_t>((sum_items + 3) / 4);
+  const int64_t blocks = n_slots * a.n_tiles + a.n_sum_blocks;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(bwd_dq_d128_kernel<HPW>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, s, a,
+                     static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v),
+                     static_cast<const bf16_t*>(dout), lse, delta, static_cast<bf16_t*>(dq));
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_bwd_mfma(const PrefillArgs& p, const void* q, const void* k, const void* v,
+                                   const void* dout, const float* lse, const float* delta, float* part,
+                                   void* dq, void* dk, void* dv, hipStream_t s) {
+  BwdArgs a = make_args(p);
+  hipError_t e;
+  if (a.g == 1)
+    e = launch_dq<1>(a, q, k, v, dout, lse, delta, dq, s);
+  else if (a.g == 2)
+    e = launch_dq<2>(a, q, k, v, dout, lse, delta, dq, s);
+  else
+    e = launch_dq<4>(a, q, k, v, dout, lse, delta, dq, s);
+  if (e != hipSuccess) return e;
+
+  const int64_t nbh = static_cast<int64_t>(a.batch) * a.hkv;
+  int64_t per_head = 0;
+  if (a.mode == KSA_MODE_KSA)
+    for (int u = 0; u < a.nu; ++u) per_head += seg_tiles_host(a, u);
+  a.n_sum_wg = static_cast<int32_t>(per_head * nbh);
+  const int64_t text_wg = nbh * ((a.n + KW - 1) / KW);
+  hipLaunchKernelGGL(bwd_dkdv_d128_kernel, dim3(static_cast<uint32_t>(a.n_sum_wg + text_wg)), dim3(256), 0, s, a,
+                     static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v),
+                     static_cast<const bf16_t*>(dout), lse, delta, static_cast<bf16_t*>(dk),
+                     static_cast<bf16_t*>(dv), part);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t items = nbh * a.M;
+  if (items == 0) return hipSuccess;
+  hipLaunchKernelGGL(bwd_sum_keys_kernel, dim3(static_cast<uint32_t>((items + 3) / 4)), dim3(256), 0, s, a,
+                     static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v),
+                     static_cast<const bf16_t*>(dout), lse, delta, part, static_cast<bf16_t*>(dk),
+                     static_cast<bf16_t*>(dv));
+  return hipGetLastError();
+}
+
+}  // namespace ksa

@@ -40,24 +40,18 @@
 //     sit on one XCD so that its K/V stay in that XCD's L2.
 #include <type_traits>
 
-#include "ksa_common.h"
 #include "ksa_internal.h"
+#include "ksa_mfma_common.h"
 
 namespace ksa {
 
 namespace {
 
-constexpr int D = 128;
+using namespace mfma;
+
 constexpr int BN = 64;            // keys per tile
-constexpr int ROW_BYTES = D * 2;  // 256 B per key row
 constexpr int TILE_BYTES = BN * ROW_BYTES;
 constexpr float kLazyRescale = 8.f;  // log2 units
-
-typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 
 struct MfmaArgs {
   int32_t batch, n, L, k, C, hq, hkv, g, M;
@@ -69,31 +63,9 @@ struct MfmaArgs {
 };
 
 __device__ __forceinline__ int32_t div_k(const MfmaArgs& a, int32_t t) {
-  return static_cast<int32_t>((__umulhi(static_cast<uint32_t>(t), a.divk_m) + static_cast<uint32_t>(t)) >>
-                              a.divk_l);
+  return fast_div_apply(t, a.divk_m, a.divk_l);
 }
 __device__ __forceinline__ int32_t trow(const MfmaArgs& a, int32_t t) { return t + div_k(a, t); }
-
-// 16-byte chunk c (0..15) of LDS row `row` is stored at chunk c ^ swz(row):
-// 8 consecutive rows hit 8 different even chunks and the next 8 the odd
-// ones, so MFMA operand reads (32 rows x 16 B) and transposing reads
-// (4 rows x 32 B per 16 lanes) spread over the banks.
-__device__ __forceinline__ int lds_off(int row, int chunk) {
-  const int swz = ((row & 7) << 1) | ((row >> 3) & 1);
-  return row * ROW_BYTES + ((chunk ^ swz) << 4);
-}
-
-__device__ __forceinline__ bf16x4_t lds_read_tr(const char* base, int byte_off) {
-  auto p = (lds_bf16x4_t*)((__attribute__((address_space(3))) char*)(base) + byte_off);
-  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p);
-}
-
-__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
-}
-
-__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // Summary query rows: one wave per (sequence, kv head, summary j) attends
 // the group's query heads to the k + 1 rows j(k+1) .. j(k+1)+k.  Lane
@@ -102,9 +74,6 @@ __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 
 // used, so a pass costs one memory round trip.
 constexpr int SUM_R = 16;  // key rows per pass
 
-// Takes the word by value: __builtin_bit_cast applied directly to a vector
-// element (v.y) reads element 0 with this compiler.
-__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2_t, w); }
 __device__ void summary_rows_wave(const MfmaArgs& a, int64_t item, const bf16_t* __restrict__ q,
                                   const bf16_t* __restrict__ kx, const bf16_t* __restrict__ vx,
                                   bf16_t* __restrict__ out, float* __restrict__ lse) {
@@ -499,13 +468,6 @@ bool prefill_mfma_supported(const PrefillArgs& a, int32_t dtype) {
                     static_cast<int64_t>(a.batch) * a.hkv * g * ((a.n_text + 31) / 32) < (int64_t(1) << 31);
   return dtype == KSA_DTYPE_BF16 && a.dqk == D && a.dv == D && !a.v_is_k_prefix && fits &&
          (g == 1 || g == 2 || g % 4 == 0);
-}
-
-static void fast_div(uint32_t d, uint32_t* m, uint32_t* l) {
-  uint32_t s = 0;
-  while ((uint64_t(1) << s) < d) ++s;
-  *l = s;
-  *m = static_cast<uint32_t>(((uint64_t(1) << 32) * ((uint64_t(1) << s) - d)) / d + 1);
 }
 
 template <int HPW>

@@ -77,3 +77,21 @@ def test_bwd_fp32_generic_k1_wide_window():
 
 def test_bwd_bf16_generic_d64():
     _case(torch.bfloat16, 64, 260, 4, 3, 4, 4, O.MODE_KSA, 0, 1, 9)
+
+
+# bf16, Dqk = Dv = 128: the MFMA dq / dkdv / summary-key kernels.  Cases span
+# several 64-row tiles and 128-key workgroups, ragged tails (n % k, n % 64),
+# the group sizes 1, 2, 4, chunk sizes 1, 5, 8, every mode, and a sequence
+# long enough that the summary keys are cut into several query segments.
+@pytest.mark.parametrize("n,k,C,hq,hkv,mode,W,batch", [
+    (300, 8, 3, 8, 2, O.MODE_KSA, 0, 1),
+    (333, 4, 5, 4, 4, O.MODE_KSA, 0, 2),
+    (700, 5, 2, 4, 2, O.MODE_KSA, 0, 1),
+    (400, 1, 20, 4, 4, O.MODE_KSA, 0, 1),
+    (1000, 8, 4, 8, 2, O.MODE_SCA, 0, 1),
+    (1000, 8, 4, 8, 2, O.MODE_SWA, 129, 1),
+    (2100, 8, 16, 16, 4, O.MODE_KSA, 0, 1),
+    (5000, 8, 4, 8, 2, O.MODE_KSA, 0, 1),
+])
+def test_bwd_bf16_mfma(n, k, C, hq, hkv, mode, W, batch):
+    _case(torch.bfloat16, 128, n, k, C, hq, hkv, mode, W, batch, 1000 + n + mode)
