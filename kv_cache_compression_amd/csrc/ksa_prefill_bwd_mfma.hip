@@ -368,7 +368,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_d128_kernel(
 // ---------------------------------------------------------------------------
 // dk, dv: keys fixed per workgroup, query tiles streamed.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256, 1) bwd_dkdv_d128_kernel(
+__global__ void __launch_bounds__(256, 2) bwd_dkdv_d128_kernel(
     BwdArgs a, const bf16_t* __restrict__ q, const bf16_t* __restrict__ kx, const bf16_t* __restrict__ vx,
     const bf16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, float* __restrict__ part) {
@@ -435,12 +435,21 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_d128_kernel(
       vop[ks] = *reinterpret_cast<const bf16x8_t*>(vx + o + 16 * ks);
     }
   }
-  // visibility bounds of the lane's key (text keys): queries [key, khi]
-  const int kc = sum_keys ? 0 : div_k(a, key_valid ? key : key0);
-  const int khi = !key_valid ? -1
-                  : sum_keys ? a.n - 1
-                  : a.mode == KSA_MODE_SWA ? key + a.W - 1
-                                           : (kc + a.C + 1) * a.k - 1;
+  // Queries that see the lane's key, as index ranges of each query kind:
+  // text queries [tq_lo, tq_hi], summary queries [sq_lo, sq_hi].
+  //   text key x, chunk c:  text x .. (c+C+1)k - 1 (or x + W - 1), summary c
+  //   summary key j:        text (j+C+1)k .. n - 1
+  const int kc = div_k(a, key_valid ? key : key0);
+  int tq_lo, tq_hi, sq_lo = 0, sq_hi = -1;
+  if (sum_keys) {
+    tq_lo = (key + a.C + 1) * a.k;
+    tq_hi = key_valid ? qt1 - 1 : -1;
+  } else {
+    tq_lo = key;
+    tq_hi = !key_valid ? -1 : min(qt1 - 1, a.mode == KSA_MODE_SWA ? key + a.W - 1 : (kc + a.C + 1) * a.k - 1);
+    sq_lo = kc;
+    sq_hi = key_valid && kc <= cs1 ? kc : -1;
+  }
   // wave-uniform: the smallest key's upper bound, the largest key
   const int kwl = min(kw0 + 31, key0 + nkeys - 1);
   const int whi_min = sum_keys ? 0 : a.mode == KSA_MODE_SWA ? kw0 + a.W - 1 : (div_k(a, kw0) + a.C + 1) * a.k - 1;
@@ -527,22 +536,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_d128_kernel(
     (void)h;
     const char* ql = lds_q[cur];
     const char* gl = lds_g[cur];
-    f32x16_t s[2], dp[2];
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[blk][r] = dp[blk][r] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        const int off = (qoff0 ^ (ks << 5)) + 32 * ROW_BYTES * blk;
-        const bf16x8_t qa_ = *reinterpret_cast<const bf16x8_t*>(ql + off);
-        const bf16x8_t ga_ = *reinterpret_cast<const bf16x8_t*>(gl + off);
-        s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa_, kop[ks], s[blk], 0, 0, 0);
-        dp[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga_, vop[ks], dp[blk], 0, 0, 0);
-      }
-    // visibility of (query row 32 blk + 8 (r / 4) + 4 half + r % 4, lane's key)
+    const float* st = &lds_st[cur][0][0];
     // full: every row of the tile is a query of the run and sees every key
     // of the wave (the first row the largest key, the last row the smallest)
     bool full;
@@ -552,26 +546,33 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_d128_kernel(
       full = i0 + BN - 1 < qt1 && kwl <= div_k(a, i0) - a.C - 1;
     else
       full = i0 + BN - 1 < qt1 && i0 >= kwl && i0 + BN - 1 <= whi_min;
-    if (!full) {
+    const int base = i0 + 4 * half;
+    const int lo = (sq ? sq_lo : tq_lo) - base;
+    const int hi = (sq ? sq_hi : tq_hi) - base;
+    // two halves of 32 query rows, one after the other (keeps the live
+    // registers within two waves per SIMD)
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
+    for (int blk = 0; blk < 2; ++blk) {
+      f32x16_t s, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const int off = (qoff0 ^ (ks << 5)) + 32 * ROW_BYTES * blk;
+        const bf16x8_t qa_ = *reinterpret_cast<const bf16x8_t*>(ql + off);
+        const bf16x8_t ga_ = *reinterpret_cast<const bf16x8_t*>(gl + off);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa_, kop[ks], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga_, vop[ks], dp, 0, 0, 0);
+      }
+      // visibility of (query row 32 blk + 8 (r / 4) + 4 half + r % 4, lane's key)
+      if (!full) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int qi = i0 + 32 * blk + 8 * (r >> 2) + 4 * half + (r & 3);
-          bool vis;
-          if (sq)
-            vis = qi <= cs1 && div_k(a, key) == qi && key_valid;
-          else if (sum_keys)
-            vis = qi < qt1 && key <= div_k(a, qi) - a.C - 1 && key_valid;
-          else
-            vis = qi < qt1 && qi >= key && qi <= khi;
-          s[blk][r] = vis ? s[blk][r] : kNegInf;
+          const int off = 32 * blk + 8 * (r >> 2) + (r & 3);
+          s[r] = (off >= lo && off <= hi) ? s[r] : kNegInf;
         }
-    }
-    const float* st = &lds_st[cur][0][0];
-    u32x4_t pw[4], dw[4];
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
+      }
+      u32x4_t pw[2], dw[2];
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int row = 32 * blk + 8 * r4 + 4 * half;
@@ -580,31 +581,33 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_d128_kernel(
         float p[4], ds[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          p[e] = fast_exp2(s[blk][4 * r4 + e] * a.sl - l4[e]);
-          ds[e] = p[e] * (dp[blk][4 * r4 + e] - d4[e]);
+          p[e] = fast_exp2(s[4 * r4 + e] * a.sl - l4[e]);
+          ds[e] = p[e] * (dp[4 * r4 + e] - d4[e]);
         }
-        // query k-slots of step ks = 2 blk + r4 / 2: rows 16 ks + 4 half + {0..3}, +8
-        const int ks = 2 * blk + (r4 >> 1);
+        // query k-slots of step 2 blk + r4 / 2: rows 16 ks + 4 half + {0..3}, +8
+        const int kk = r4 >> 1;
         const int w0 = 2 * (r4 & 1);
-        pw[ks][w0] = pk_bf16(p[0], p[1]);
-        pw[ks][w0 + 1] = pk_bf16(p[2], p[3]);
-        dw[ks][w0] = pk_bf16(ds[0], ds[1]);
-        dw[ks][w0 + 1] = pk_bf16(ds[2], ds[3]);
+        pw[kk][w0] = pk_bf16(p[0], p[1]);
+        pw[kk][w0 + 1] = pk_bf16(p[2], p[3]);
+        dw[kk][w0] = pk_bf16(ds[0], ds[1]);
+        dw[kk][w0 + 1] = pk_bf16(ds[2], ds[3]);
       }
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, pw[ks]);
-      const bf16x8_t dop = __builtin_bit_cast(bf16x8_t, dw[ks]);
+      for (int kk = 0; kk < 2; ++kk) {
+        const int ks = 2 * blk + kk;
+        const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, pw[kk]);
+        const bf16x8_t dop = __builtin_bit_cast(bf16x8_t, dw[kk]);
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const bf16x4_t glo = lds_read_tr(gl, toff[0][db] + 16 * ROW_BYTES * ks);
-        const bf16x4_t ghi = lds_read_tr(gl, toff[1][db] + 16 * ROW_BYTES * ks);
-        dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_shufflevector(glo, ghi, 0, 1, 2, 3, 4, 5, 6, 7),
-                                                            pop, dvacc[db], 0, 0, 0);
-        const bf16x4_t qlo = lds_read_tr(ql, toff[0][db] + 16 * ROW_BYTES * ks);
-        const bf16x4_t qhi = lds_read_tr(ql, toff[1][db] + 16 * ROW_BYTES * ks);
-        dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7),
-                                                            dop, dkacc[db], 0, 0, 0);
+        for (int db = 0; db < 4; ++db) {
+          const bf16x4_t glo = lds_read_tr(gl, toff[0][db] + 16 * ROW_BYTES * ks);
+          const bf16x4_t ghi = lds_read_tr(gl, toff[1][db] + 16 * ROW_BYTES * ks);
+          dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_shufflevector(glo, ghi, 0, 1, 2, 3, 4, 5, 6, 7), pop, dvacc[db], 0, 0, 0);
+          const bf16x4_t qlo = lds_read_tr(ql, toff[0][db] + 16 * ROW_BYTES * ks);
+          const bf16x4_t qhi = lds_read_tr(ql, toff[1][db] + 16 * ROW_BYTES * ks);
+          dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7), dop, dkacc[db], 0, 0, 0);
+        }
       }
     }
     if (it + 1 < n_total && tid < 2 * BN) lds_st[cur ^ 1][tid >> 6][tid & (BN - 1)] = st_next;
