@@ -216,6 +216,7 @@ def main() -> int:
         if any(errs):
             raise RuntimeError(f"decode cache error bits {errs}")
     long_runs = [] if args.no_long else prefill_long(ksa, ksa_synth, torch, dev, stream)
+    bwd = prefill_backward(ksa, ksa_synth, torch, w, p, qd, kd, vd, stream)
     # the report's summary-free baselines on the same inputs (A/B timing)
     modes = []
     for mode, name, W in ((ksa.MODE_SCA, "sliding chunks (no summaries)", 0),
@@ -269,6 +270,7 @@ def main() -> int:
                        "slice_rows_total": mla_rows, "bytes": mla_bytes},
         "prefill_long": long_runs,
         "prefill_baselines": modes,
+        "prefill_backward": bwd,
         "rope": {"value": round(rope_gbps, 1), "unit": "GB/s", "ms": round(seg_ms["rope"], 4)},
         "breakdown_ms": {s: round(v, 4) for s, v in seg_ms.items()},
         "roofline": {"kernel": "prefill_mfma_d128_kernel", "bound": "mfma", "achieved": round(pre_tflops, 2),
@@ -358,6 +360,36 @@ def prefill_long(ksa, ksa_synth, torch, dev, stream, reps: int = 5) -> list:
         del qd, kd, vd, out
         torch.cuda.empty_cache()
     return res
+
+
+def prefill_backward(ksa, ksa_synth, torch, w, p, qd, kd, vd, stream, reps: int = 5) -> dict:
+    """Backward of the prefill on the same workload and inputs: dq, dk, dv
+    from a seeded output gradient, the forward's output and normaliser."""
+    L = ksa.ksa_augmented_len(w.n_text, w.chunk)
+    g = ksa_synth.normal((w.batch, L, w.hq, w.dv), w.dtype, ksa_synth.gen(w.seed + 7)).to(qd.device)
+    lse = torch.empty((w.batch, w.hq, L), dtype=torch.float32, device=qd.device)
+    out = ksa.ksa_prefill_attn(p, qd, kd, vd, w.n_text, lse=lse, stream=stream)
+    ws = torch.empty(ksa.ksa_prefill_bwd_workspace_bytes(p, w.batch, w.n_text), dtype=torch.uint8,
+                     device=qd.device)
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+    run = lambda: ksa.ksa_prefill_attn_bwd(p, ksa.MODE_KSA, 0, qd, kd, vd, out, g, lse, w.n_text,
+                                           dq, dk, dv, ws, stream=stream)
+    run()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(reps):
+        run()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / reps
+    # recompute S, dP, then dV, dK, dQ: five products over every visible pair
+    fl = 2 * (3 * w.dqk + 2 * w.dv) * w.hq * visible_pairs(w.n_text, w.chunk, w.window) * w.batch
+    tf = fl / (ms * 1e-3) / 1e12
+    del g, lse, out, ws, dq, dk, dv
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "ms": round(ms, 4), "tflops": round(tf, 2),
+            "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4), "flops": fl,
+            "workspace_mb": round(ksa.ksa_prefill_bwd_workspace_bytes(p, w.batch, w.n_text) / 1e6, 1)}
 
 
 def cpu_baseline(w, rows_req: int) -> dict:

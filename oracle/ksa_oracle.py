@@ -391,6 +391,34 @@ def attention_backward(q: np.ndarray, kx: np.ndarray, v: np.ndarray, dout: np.nd
     return dq, dk, dvv
 
 
+def attention_backward_rows(q: np.ndarray, kx: np.ndarray, v: np.ndarray, dout: np.ndarray,
+                            n: int, k: int, scale: float, rows: Sequence[int], mode: int = MODE_KSA,
+                            C: int = 0, W: int = 0, heads: Optional[Sequence[int]] = None
+                            ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """The terms of :func:`attention_backward` that come from the query rows
+    ``rows`` (query heads ``heads``, default all): dq of those rows
+    [R, Hq', Dqk] and their contributions to dk, dv of every key
+    [L, Hkv, D].  Summed over all rows and heads it is the full backward;
+    restricted to the rows that see a key, it is that key's exact gradient.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    Hq = q.shape[1]
+    Hkv = kx.shape[1]
+    g = Hq // Hkv
+    heads = list(range(Hq)) if heads is None else list(heads)
+    mask = baseline_mask(n, k, mode, C, W, rows=rows)
+    dq = np.zeros((len(rows), len(heads), q.shape[2]))
+    dk = np.zeros(kx.shape)
+    dvv = np.zeros(v.shape)
+    for hi, h in enumerate(heads):
+        a, b, c = attention_masked_backward(q[rows, h], kx[:, h // g], v[:, h // g], mask, scale,
+                                            dout[rows, h])
+        dq[:, hi] = a
+        dk[:, h // g] += b
+        dvv[:, h // g] += c
+    return dq, dk, dvv
+
+
 def visible_pairs_bruteforce(n: int, k: int, C: int,
                              summary_sees_self: bool = True) -> int:
     return int(visibility_mask_fast(n, k, C, summary_sees_self).sum())

@@ -91,3 +91,23 @@ def test_reduces_to_causal_autograd(n, k, hq, hkv):
     np.testing.assert_allclose(dk[txt], tk.grad.numpy().transpose(1, 0, 2), atol=1e-12)
     np.testing.assert_allclose(dv[txt], tv.grad.numpy().transpose(1, 0, 2), atol=1e-12)
     assert np.all(dk[is_s] == 0.0) and np.all(dv[is_s] == 0.0)
+
+
+def test_rows_split_sums_to_full_backward():
+    """The per-row terms over a partition of the rows add up to the full
+    backward (each key's gradient is a sum over the queries that see it)."""
+    n, k, C = 30, 4, 1
+    q, kx, v, g = _inputs(n, k, 4, 2, 5, seed=21)
+    dq, dk, dv = O.attention_backward(q, kx, v, g, n, k, 0.6, C=C)
+    L = O.augmented_len(n, k)
+    parts = [np.arange(0, 11), np.arange(11, 20), np.arange(20, L)]
+    sk, sv = np.zeros_like(dk), np.zeros_like(dv)
+    for rows in parts:
+        a, b, c = O.attention_backward_rows(q, kx, v, g, n, k, 0.6, rows, C=C)
+        np.testing.assert_allclose(a, dq[rows], atol=1e-13)
+        sk += b
+        sv += c
+    np.testing.assert_allclose(sk, dk, atol=1e-12)
+    np.testing.assert_allclose(sv, dv, atol=1e-12)
+    a, _, _ = O.attention_backward_rows(q, kx, v, g, n, k, 0.6, [3, 7], C=C, heads=[1, 2])
+    np.testing.assert_allclose(a, dq[[3, 7]][:, [1, 2]], atol=1e-13)
