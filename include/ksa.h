@@ -201,6 +201,39 @@ KSA_API int32_t ksa_cache_append(const ksa_params* p, const ksa_cache* c, int32_
 KSA_API int32_t ksa_cache_fill(const ksa_params* p, const ksa_cache* c, int32_t batch, int64_t n_text,
                        const void* k_aug, const void* v_aug, void* stream);
 
+/* Append the next augmented rows of each sequence (chunked prefill hand-off,
+ * Sec. 2.3.1): sequence b continues at row m (k+1) + r of Eq. 1 (its state)
+ * with R_b = seg_rows[b+1] - seg_rows[b] rows; text rows act as kind-0
+ * appends and summary rows (every (k+1)-th row) as kind-1 appends, in order,
+ * and the result equals those single appends.
+ *   seg_rows [batch + 1] device int64, non-decreasing packed row offsets
+ *   k_rows [seg_rows[batch], Hkv, Dqk], v_rows [.., Hkv, Dv] (post-RoPE)
+ *   max_rows >= every R_b (sizes the launch).
+ * A sequence whose summaries would exceed max_summaries is left untouched
+ * and gets KSA_CACHE_ERR_SUMMARY_FULL. */
+KSA_API int32_t ksa_cache_append_rows(const ksa_params* p, const ksa_cache* c, int32_t batch,
+                              const int64_t* seg_rows, int64_t max_rows, const void* k_rows,
+                              const void* v_rows, void* stream);
+
+/* Chunked and variable-length (batched) prefill against the cache (the
+ * serving path next to the prefill hand-off of Sec. 2.3.1).  Sequence b's
+ * segment is the R_b = seg_rows[b+1] - seg_rows[b] augmented rows that
+ * follow its cache state {m, r}: rows m (k+1) + r onward of Eq. 1, text and
+ * summary rows interleaved as in the one-shot layout.  Every segment row
+ * gets the output the one-shot ksa_prefill_attn gives that row of the whole
+ * sequence (KSA rule); keys before the segment are read from the cache
+ * regions (summary buffer, ring, current chunk), which hold every key a
+ * segment row can see, and keys in the segment from k / v.
+ *   seg_rows [batch + 1] device int64, non-decreasing, seg_rows[0] = 0
+ *   q   [total_rows, Hq, Dqk]   k [total_rows, Hkv, Dqk]   v [total_rows, Hkv, Dv]
+ *   out [total_rows, Hq, Dv]    lse [Hq, total_rows] fp32 natural log, or NULL
+ *   max_rows >= every R_b, total_rows = seg_rows[batch].
+ * The cache is read only; ksa_cache_append_rows with the same seg_rows and
+ * k / v then moves the segment into it. */
+KSA_API int32_t ksa_prefill_chunk(const ksa_params* p, const ksa_cache* c, int32_t batch,
+                          const int64_t* seg_rows, int64_t max_rows, int64_t total_rows, const void* q,
+                          const void* k, const void* v, void* out, float* lse, void* stream);
+
 /* Bytes of workspace ksa_decode_attn needs for this batch and capacity. */
 KSA_API size_t ksa_decode_workspace_bytes(const ksa_params* p, int32_t batch, int32_t max_summaries);
 

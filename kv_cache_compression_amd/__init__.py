@@ -35,7 +35,7 @@ EXPORTS = (
     "ksa_status_string", "ksa_last_error_message", "ksa_augmented_len", "ksa_rope_augmented",
     "ksa_rope_positions", "ksa_prefill_attn", "ksa_prefill_attn_mode", "ksa_prefill_bwd_workspace_bytes",
     "ksa_prefill_attn_bwd", "ksa_cache_slots", "ksa_cache_reset",
-    "ksa_cache_append", "ksa_cache_fill", "ksa_decode_workspace_bytes", "ksa_decode_attn",
+    "ksa_cache_append", "ksa_cache_fill", "ksa_cache_append_rows", "ksa_prefill_chunk", "ksa_decode_workspace_bytes", "ksa_decode_attn",
     "ksa_cache_read_errors",
 )
 
@@ -95,6 +95,8 @@ _SIGS = {
     "ksa_cache_reset": (_i32, [_P, _C, _i32, _vp]),
     "ksa_cache_append": (_i32, [_P, _C, _i32, _vp, _vp, _vp, _vp]),
     "ksa_cache_fill": (_i32, [_P, _C, _i32, _i64, _vp, _vp, _vp]),
+    "ksa_cache_append_rows": (_i32, [_P, _C, _i32, _vp, _i64, _vp, _vp, _vp]),
+    "ksa_prefill_chunk": (_i32, [_P, _C, _i32, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
     "ksa_decode_workspace_bytes": (ctypes.c_size_t, [_P, _i32, _i32]),
     "ksa_decode_attn": (_i32, [_P, _C, _i32, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "ksa_cache_read_errors": (_i32, [_P, _C, _i32, _vp, _vp]),
@@ -332,6 +334,49 @@ def ksa_cache_fill(c: Cache, k_aug: torch.Tensor, v_aug: Optional[torch.Tensor],
     pc, cc = p.c(), c.c()
     _check(lib().ksa_cache_fill(ctypes.byref(pc), ctypes.byref(cc), c.batch, n_text, _ptr(k_aug),
                                 None if p.v_is_k_prefix else _ptr(v_aug), _stream(stream)))
+
+
+def _seg_rows(c: Cache, seg_rows: torch.Tensor, rows: torch.Tensor):
+    _need(seg_rows, (c.batch + 1,), torch.int64, "seg_rows")
+    total = rows.shape[0]
+    return total
+
+
+def ksa_cache_append_rows(c: Cache, seg_rows: torch.Tensor, max_rows: int, k_rows: torch.Tensor,
+                          v_rows: Optional[torch.Tensor], stream=None) -> None:
+    """Append each sequence's next augmented rows (packed at ``seg_rows``)."""
+    p = c.p
+    total = _seg_rows(c, seg_rows, k_rows)
+    _need(k_rows, (total, p.num_kv_heads, p.head_dim_qk), p.dtype, "k_rows")
+    if not p.v_is_k_prefix:
+        _need(v_rows, (total, p.num_kv_heads, p.head_dim_v), p.dtype, "v_rows")
+    pc, cc = p.c(), c.c()
+    _check(lib().ksa_cache_append_rows(ctypes.byref(pc), ctypes.byref(cc), c.batch, _ptr(seg_rows), max_rows,
+                                       _ptr(k_rows), None if p.v_is_k_prefix else _ptr(v_rows),
+                                       _stream(stream)))
+
+
+def ksa_prefill_chunk(c: Cache, seg_rows: torch.Tensor, max_rows: int, q: torch.Tensor, k: torch.Tensor,
+                      v: Optional[torch.Tensor], out: Optional[torch.Tensor] = None,
+                      lse: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Chunked / varlen prefill of each sequence's next rows against its
+    cache.  Returns ``out`` [total_rows, Hq, Dv]."""
+    p = c.p
+    total = _seg_rows(c, seg_rows, q)
+    _need(q, (total, p.num_q_heads, p.head_dim_qk), p.dtype, "q")
+    _need(k, (total, p.num_kv_heads, p.head_dim_qk), p.dtype, "k")
+    if not p.v_is_k_prefix:
+        _need(v, (total, p.num_kv_heads, p.head_dim_v), p.dtype, "v")
+    if out is None:
+        out = torch.empty((total, p.num_q_heads, p.head_dim_v), dtype=p.dtype, device=q.device)
+    _need(out, (total, p.num_q_heads, p.head_dim_v), p.dtype, "out")
+    if lse is not None:
+        _need(lse, (p.num_q_heads, total), torch.float32, "lse")
+    pc, cc = p.c(), c.c()
+    _check(lib().ksa_prefill_chunk(ctypes.byref(pc), ctypes.byref(cc), c.batch, _ptr(seg_rows), max_rows, total,
+                                   _ptr(q), _ptr(k), None if p.v_is_k_prefix else _ptr(v), _ptr(out), _ptr(lse),
+                                   _stream(stream)))
+    return out
 
 
 def ksa_decode_workspace_bytes(p: Params, batch: int, max_summaries: int) -> int:

@@ -19,6 +19,8 @@ SOURCES = [
     "ksa_prefill_mfma.hip",
     "ksa_prefill_bwd_generic.hip",
     "ksa_prefill_bwd_mfma.hip",
+    "ksa_prefill_chunk_generic.hip",
+    "ksa_prefill_chunk_mfma.hip",
     "ksa_cache.hip",
     "ksa_decode.hip",
     "ksa_decode_mla.hip",

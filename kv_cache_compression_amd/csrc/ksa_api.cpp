@@ -311,6 +311,59 @@ int32_t ksa_cache_fill(const ksa_params* p, const ksa_cache* c, int32_t batch, i
                     "cache_fill");
 }
 
+int32_t ksa_cache_append_rows(const ksa_params* p, const ksa_cache* c, int32_t batch, const int64_t* seg_rows,
+                              int64_t max_rows, const void* k_rows, const void* v_rows, void* stream) {
+  if (int32_t st = check_params(p)) return st;
+  if (int32_t st = check_cache(p, c)) return st;
+  if (batch < 0 || max_rows < 0) return fail(KSA_STATUS_INVALID_ARGUMENT, "negative batch/max_rows");
+  if (batch == 0 || max_rows == 0) return KSA_STATUS_OK;
+  if (!seg_rows || !k_rows || (!p->v_is_k_prefix && !v_rows))
+    return fail(KSA_STATUS_INVALID_ARGUMENT, "seg_rows/k_rows/v_rows is NULL");
+  g_msg[0] = 0;
+  return hip_status(ksa::launch_cache_append_rows(cache_args(p, c, batch), p->dtype, seg_rows, max_rows, c->k,
+                                                  c->v, c->state, k_rows, v_rows,
+                                                  static_cast<hipStream_t>(stream)),
+                    "cache_append_rows");
+}
+
+int32_t ksa_prefill_chunk(const ksa_params* p, const ksa_cache* c, int32_t batch, const int64_t* seg_rows,
+                          int64_t max_rows, int64_t total_rows, const void* q, const void* k, const void* v,
+                          void* out, float* lse, void* stream) {
+  if (int32_t st = check_params(p)) return st;
+  if (int32_t st = check_cache(p, c)) return st;
+  if (batch < 0 || max_rows < 0 || total_rows < 0)
+    return fail(KSA_STATUS_INVALID_ARGUMENT, "negative batch/max_rows/total_rows");
+  if (batch == 0 || max_rows == 0 || total_rows == 0) return KSA_STATUS_OK;
+  if (!seg_rows || !q || !k || !out || (!p->v_is_k_prefix && !v))
+    return fail(KSA_STATUS_INVALID_ARGUMENT, "seg_rows/q/k/v/out is NULL");
+  const int64_t slots = 1 + static_cast<int64_t>(p->chunk_size) +
+                        static_cast<int64_t>(p->window_chunks) * p->chunk_size + c->max_summaries;
+  // augmented rows of a whole sequence stay below the summary capacity's reach
+  const int64_t max_seq_rows = static_cast<int64_t>(c->max_summaries + 1) * (p->chunk_size + 1);
+  if (max_seq_rows + max_rows > (int64_t(1) << 30) || total_rows > (int64_t(1) << 31))
+    return fail(KSA_STATUS_UNSUPPORTED, "sequence or packed rows too long");
+  ksa::ChunkArgs a;
+  a.batch = batch;
+  a.k = p->chunk_size;
+  a.C = p->window_chunks;
+  a.hq = p->num_q_heads;
+  a.hkv = p->num_kv_heads;
+  a.dqk = p->head_dim_qk;
+  a.dv = p->head_dim_v;
+  a.v_is_k_prefix = p->v_is_k_prefix;
+  a.scale = p->softmax_scale;
+  a.slots = slots;
+  a.max_rows = max_rows;
+  a.total_rows = total_rows;
+  ksa::ChunkPtrs ptrs{c->k, p->v_is_k_prefix ? nullptr : c->v, c->state, seg_rows, q, k,
+                      p->v_is_k_prefix ? nullptr : v, out, lse};
+  g_msg[0] = 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (ksa::prefill_chunk_mfma_supported(a, p->dtype))
+    return hip_status(ksa::launch_prefill_chunk_mfma(a, ptrs, s), "prefill_chunk");
+  return hip_status(ksa::launch_prefill_chunk_generic(a, p->dtype, ptrs, s), "prefill_chunk");
+}
+
 size_t ksa_decode_workspace_bytes(const ksa_params* p, int32_t batch, int32_t max_summaries) {
   if (check_params(p) || batch < 0 || max_summaries < 0) return 0;
   return ksa::decode_workspace_bytes(decode_args(p, batch, max_summaries));

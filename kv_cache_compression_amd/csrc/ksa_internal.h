@@ -57,6 +57,32 @@ hipError_t launch_prefill_bwd_mfma(const PrefillArgs& a, const void* q, const vo
                                    const void* dout, const float* lse, const float* delta, float* part,
                                    void* dq, void* dk, void* dv, hipStream_t s);
 
+// Chunked / varlen prefill against the cache: sequence b's segment is the
+// R_b = seg_rows[b+1] - seg_rows[b] augmented rows that follow its cache
+// state {m, r} (rows a0 = m (k+1) + r onward), packed at row seg_rows[b].
+struct ChunkArgs {
+  int32_t batch, k, C, hq, hkv, dqk, dv;
+  int32_t v_is_k_prefix;
+  float scale;
+  int64_t slots;       // cache slots per (sequence, kv head)
+  int64_t max_rows;    // >= every R_b
+  int64_t total_rows;  // packed rows: the lse row stride
+};
+struct ChunkPtrs {
+  const void* ck;  // cache K [batch, Hkv, slots, Dqk]
+  const void* cv;  // cache V (nullptr when V is a K prefix)
+  const int32_t* state;
+  const int64_t* seg_rows;
+  const void* q;   // [total_rows, Hq, Dqk]
+  const void* k;   // [total_rows, Hkv, Dqk]
+  const void* v;   // [total_rows, Hkv, Dv] (nullptr when V is a K prefix)
+  void* out;       // [total_rows, Hq, Dv]
+  float* lse;      // [Hq, total_rows] or nullptr
+};
+hipError_t launch_prefill_chunk_generic(const ChunkArgs& a, int32_t dtype, const ChunkPtrs& p, hipStream_t s);
+bool prefill_chunk_mfma_supported(const ChunkArgs& a, int32_t dtype);
+hipError_t launch_prefill_chunk_mfma(const ChunkArgs& a, const ChunkPtrs& p, hipStream_t s);
+
 struct CacheArgs {
   int32_t batch, k, C, hkv, dqk, dv;
   int32_t v_is_k_prefix;
@@ -68,6 +94,9 @@ hipError_t launch_cache_reset(const CacheArgs& a, int32_t* state, hipStream_t s)
 hipError_t launch_cache_append(const CacheArgs& a, int32_t dtype, void* ck, void* cv,
                                int32_t* state, const void* k_new, const void* v_new,
                                const int32_t* kind, hipStream_t s);
+hipError_t launch_cache_append_rows(const CacheArgs& a, int32_t dtype, const int64_t* seg_rows, int64_t max_rows,
+                                    void* ck, void* cv, int32_t* state, const void* k_rows, const void* v_rows,
+                                    hipStream_t s);
 hipError_t launch_cache_fill(const CacheArgs& a, int32_t dtype, int64_t n_text, void* ck, void* cv,
                              int32_t* state, const void* k_aug, const void* v_aug, hipStream_t s);
 

@@ -1,0 +1,461 @@
+// Chunked (and variable-length, batched) KSA prefill against the cache for
+// bf16, Dqk = Dv = 128, on gfx950 MFMA.
+//
+// A sequence with m committed chunks and r current-chunk tokens in its
+// cache ("Kwai Summary Attention Technical Report", Sec. 2.3.1, Fig. 4)
+// continues at augmented row a0 = m (k+1) + r of Eq. (1); its segment is
+// the next R rows, packed with the other sequences' segments.  Every
+// segment row gets exactly the output of the one-shot prefill (Eq. 3 and
+// the summary rule).  The keys of a block of text queries are, as in the
+// one-shot kernel, a summary run and a text run, each contiguous in its own
+// index space; here each run is cut where the cache ends and the segment
+// begins, giving up to four runs walked in 64-key tiles:
+//   summaries j < m        cache summary buffer, slot 1 + k + C k + j;
+//   summaries j >= m       segment rows;
+//   text before the segment  the current chunk (token o at slot k - o) or
+//                          ring chunk slot c mod C (token o at k - 1 - o);
+//   text in the segment    segment rows.
+// A tile never mixes sources, so each tile has one buffer resource and the
+// loads stay direct-to-LDS; a run's last tile masks keys past the run's
+// end.  The compute pipeline is the one-shot kernel's: S^T = K Q^T and
+// O^T += V^T P^T on v_mfma_f32_32x32x16_bf16, lazy rescale, one barrier
+// per tile.  Summary query rows of the segments run in the first
+// workgroups, one wave per (sequence, kv head, summary).
+#include <type_traits>
+
+#include "ksa_internal.h"
+#include "ksa_mfma_common.h"
+
+namespace ksa {
+
+namespace {
+
+using namespace mfma;
+
+constexpr int BN = 64;
+constexpr int TILE_BYTES = BN * ROW_BYTES;
+constexpr float kLazyRescale = 8.f;  // log2 units
+constexpr int SLOT_BYTES = ROW_BYTES; // one (slot, kv head) row of the cache
+
+struct CkArgs {
+  int32_t batch, k, C, hq, hkv, g, n_hg, n_tiles;
+  uint32_t divk_m, divk_l;
+  float sl;
+  int32_t slots, sum0;  // cache slots per (sequence, kv head); first summary slot
+  int32_t max_rows, max_sum_seg, n_sum_blocks;
+  int64_t total_rows;
+};
+
+__device__ __forceinline__ int32_t div_k(const CkArgs& a, int32_t t) { return fast_div_apply(t, a.divk_m, a.divk_l); }
+__device__ __forceinline__ int32_t trow(const CkArgs& a, int32_t t) { return t + div_k(a, t); }
+
+// Cache slot of history text x (chunk cx <= m).
+__device__ __forceinline__ int32_t text_slot(const CkArgs& a, int32_t x, int32_t m) {
+  const int32_t cx = div_k(a, x);
+  const int32_t ox = x - cx * a.k;
+  if (cx == m) return a.k - ox;
+  return 1 + a.k + (a.C > 0 ? cx % a.C : 0) * a.k + (a.k - 1 - ox);
+}
+
+// Summary query s_j of a segment: its chunk's k text keys and itself.  Lane
+// (hh, c) holds dims 8c .. 8c+7 of head hh of a group of four.
+__device__ void chunk_summary_wave(const CkArgs& a, int64_t item, const ChunkPtrs& p) {
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 15;
+  const int hh = lane >> 4;
+  const int jl = static_cast<int>(item % a.max_sum_seg);
+  const int kvh = static_cast<int>((item / a.max_sum_seg) % a.hkv);
+  const int b = static_cast<int>(item / (static_cast<int64_t>(a.max_sum_seg) * a.hkv));
+  const int m = p.state[4 * b], r = p.state[4 * b + 1];
+  const int64_t off = p.seg_rows[b];
+  const int a0 = m * (a.k + 1) + r;
+  const int a1 = a0 + static_cast<int>(p.seg_rows[b + 1] - off);
+  const int j = m + jl;
+  if (j >= a1 / (a.k + 1)) return;
+  const int t_seg = a0 - a0 / (a.k + 1);
+  const int srow = j * (a.k + 1) + a.k;
+  const bf16_t* ckb = static_cast<const bf16_t*>(p.ck) + (static_cast<int64_t>(b) * a.hkv + kvh) * a.slots * D + 8 * c;
+  const bf16_t* cvb = static_cast<const bf16_t*>(p.cv) + (static_cast<int64_t>(b) * a.hkv + kvh) * a.slots * D + 8 * c;
+  const int64_t kvs = static_cast<int64_t>(a.hkv) * D;
+  const bf16_t* skb = static_cast<const bf16_t*>(p.k) + (off - a0) * kvs + kvh * D + 8 * c;
+  const bf16_t* svb = static_cast<const bf16_t*>(p.v) + (off - a0) * kvs + kvh * D + 8 * c;
+  const bf16_t* qb = static_cast<const bf16_t*>(p.q);
+  for (int hg = 0; hg < a.g; hg += 4) {
+    const int hloc = hg + hh;
+    const bool hval = hloc < a.g;
+    const int h = kvh * a.g + (hval ? hloc : 0);
+    const int64_t qrow = off + srow - a0;
+    const u32x4_t qw = *reinterpret_cast<const u32x4_t*>(qb + (qrow * a.hq + h) * D + 8 * c);
+    float m_run = kNegInf, l = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int e = 0; e <= a.k; ++e) {
+      const bf16_t *kp, *vp;
+      if (e == a.k) {
+        kp = skb + static_cast<int64_t>(srow) * kvs;
+        vp = svb + static_cast<int64_t>(srow) * kvs;
+      } else {
+        const int x = j * a.k + e;
+        if (x < t_seg) {  // chunk m, still in the current region
+          kp = ckb + static_cast<int64_t>(a.k - e) * D;
+          vp = cvb + static_cast<int64_t>(a.k - e) * D;
+        } else {
+          kp = skb + static_cast<int64_t>(x + j) * kvs;
+          vp = svb + static_cast<int64_t>(x + j) * kvs;
+        }
+      }
+      const u32x4_t kw = *reinterpret_cast<const u32x4_t*>(kp);
+      const u32x4_t vw = *reinterpret_cast<const u32x4_t*>(vp);
+      float part = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        part = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qw[w]), as_bf16x2(kw[w]), part, false);
+      part += __shfl_xor(part, 8);
+      part += __shfl_xor(part, 4);
+      part += __shfl_xor(part, 2);
+      part += __shfl_xor(part, 1);
+      const float sc = part * a.sl;
+      const float mx = fmaxf(m_run, sc);
+      const float al = m_run == kNegInf ? 0.f : fast_exp2(m_run - mx);
+      const float pr = fast_exp2(sc - mx);
+      l = l * al + pr;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        o[2 * w] = o[2 * w] * al + pr * bf_lo(vw[w]);
+        o[2 * w + 1] = o[2 * w + 1] * al + pr * bf_hi(vw[w]);
+      }
+      m_run = mx;
+    }
+    if (hval) {
+      const float inv = 1.f / l;
+      u32x4_t ow;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) ow[w] = pk_bf16(o[2 * w] * inv, o[2 * w + 1] * inv);
+      *reinterpret_cast<u32x4_t*>(static_cast<bf16_t*>(p.out) + (qrow * a.hq + h) * D + 8 * c) = ow;
+      if (p.lse && c == 0) p.lse[static_cast<int64_t>(h) * a.total_rows + qrow] = (m_run + log2f(l)) * kLn2;
+    }
+  }
+}
+
+}  // namespace
+
+template <int HPW>
+__global__ void __launch_bounds__(256, 2) prefill_chunk_d128_kernel(CkArgs a, ChunkPtrs p) {
+  constexpr int PT = 32 * (4 / HPW);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (static_cast<int>(blockIdx.x) < a.n_sum_blocks) {
+    const int64_t item = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+    if (item < static_cast<int64_t>(a.batch) * a.hkv * a.max_sum_seg) chunk_summary_wave(a, item, p);
+    return;
+  }
+  const int n_slots = a.batch * a.hkv * a.n_hg;
+  const int bid = blockIdx.x - a.n_sum_blocks;
+  const int hslot = bid % n_slots;
+  const int tile = bid / n_slots;
+  const int hg = hslot % a.n_hg;
+  const int kvh = (hslot / a.n_hg) % a.hkv;
+  const int b = hslot / (a.n_hg * a.hkv);
+  const int h = kvh * a.g + hg * HPW + (wave % HPW);
+
+  const int m = __builtin_amdgcn_readfirstlane(p.state[4 * b]);
+  const int r = __builtin_amdgcn_readfirstlane(p.state[4 * b + 1]);
+  const int64_t off = p.seg_rows[b];
+  const int R = static_cast<int>(p.seg_rows[b + 1] - off);
+  const int a0 = m * (a.k + 1) + r, a1 = a0 + R;
+  const int t_seg = a0 - a0 / (a.k + 1), t_end = a1 - a1 / (a.k + 1);  // segment text [t_seg, t_end)
+  const int p0 = (t_seg / PT) * PT + tile * PT;
+  if (p0 >= t_end) return;
+  const int qlo = p0 > t_seg ? p0 : t_seg;
+  const int p_last = (p0 + PT < t_end ? p0 + PT : t_end) - 1;
+  const int c_first = div_k(a, qlo), c_last = div_k(a, p_last);
+  const int sn = c_last - a.C > 0 ? c_last - a.C : 0;
+  const int t0 = c_first - a.C > 0 ? (c_first - a.C) * a.k : 0;
+  // runs: [0, e0) cache summaries, [m, sn) segment summaries,
+  //       [t0, e2) cache text, [s3, p_last] segment text
+  const int e0 = sn < m ? sn : m;
+  const int len1 = sn - m > 0 ? sn - m : 0;
+  const int e2 = p_last + 1 < t_seg ? p_last + 1 : t_seg;
+  const int len2 = e2 - t0 > 0 ? e2 - t0 : 0;
+  const int s3 = t0 > t_seg ? t0 : t_seg;
+  const int n0 = (e0 + BN - 1) / BN, n1 = (len1 + BN - 1) / BN, n2 = (len2 + BN - 1) / BN;
+  const int n01 = n0 + n1, n012 = n01 + n2;
+  const int n_total = n012 + (p_last - s3 + BN) / BN;
+
+  const int iw0 = p0 + 32 * (wave / HPW);
+  const int iw0v = iw0 > t_seg ? iw0 : t_seg;  // first valid query of the wave
+  const int iw1 = iw0 + 31 < p_last ? iw0 + 31 : p_last;
+  const bool wave_active = iw0v <= iw1;
+  const int qi = iw0 + (lane & 31);
+  const bool q_valid = qi >= t_seg && qi <= p_last;
+  const int ci = div_k(a, q_valid ? qi : t_seg);
+  const int smax = q_valid ? ci - a.C - 1 : -1;
+  const int tlo = q_valid ? (ci - a.C > 0 ? (ci - a.C) * a.k : 0) : 0x7fffffff;
+  const int cw0 = div_k(a, wave_active ? iw0v : t_seg), cw1 = div_k(a, wave_active ? iw1 : t_seg);
+  const int tlo_w1 = cw1 - a.C > 0 ? (cw1 - a.C) * a.k : 0;
+
+  const int half = lane >> 5;
+  const int64_t qrow = off + (q_valid ? trow(a, qi) : t_seg + div_k(a, t_seg)) - a0;
+  bf16x8_t qop[8];
+  {
+    const bf16_t* qp = static_cast<const bf16_t*>(p.q) + (qrow * a.hq + h) * D + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qop[ks] = q_valid ? *reinterpret_cast<const bf16x8_t*>(qp + 16 * ks) : bf16x8_t{};
+  }
+
+  const int ld_chunk = tid & 15;
+  const int ld_row = tid >> 4;
+  const int RB = a.hkv * D * 2;  // bytes per segment row
+  const int chunk16 = 16 * (ld_chunk ^ lds_swz(ld_row));
+  const int64_t cbase = (static_cast<int64_t>(b) * a.hkv + kvh) * a.slots * D;
+  const int cbytes = a.slots * SLOT_BYTES;
+  const int64_t sbase = off * a.hkv * D + kvh * D;
+  const int sbytes = R * RB - kvh * D * 2;
+  const __amdgpu_buffer_rsrc_t rc_k = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(static_cast<const void*>(static_cast<const bf16_t*>(p.ck) + cbase)), static_cast<short>(0), cbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rc_v = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(static_cast<const void*>(static_cast<const bf16_t*>(p.cv) + cbase)), static_cast<short>(0), cbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs_k = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(static_cast<const void*>(static_cast<const bf16_t*>(p.k) + sbase)), static_cast<short>(0), sbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs_v = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(static_cast<const void*>(static_cast<const bf16_t*>(p.v) + sbase)), static_cast<short>(0), sbytes, 0x00020000);
+  __shared__ __attribute__((aligned(16))) char lds_k0[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char lds_k1[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char lds_v0[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char lds_v1[TILE_BYTES];
+  char* const lds_k[2] = {lds_k0, lds_k1};
+  char* const lds_v[2] = {lds_v0, lds_v1};
+  // tile tt -> run (0..3), first key, run end (exclusive)
+  auto tile_run = [&](int tt, int* run, int* key0, int* kend) {
+    if (tt < n0) {
+      *run = 0; *key0 = tt * BN; *kend = e0;
+    } else if (tt < n01) {
+      *run = 1; *key0 = m + (tt - n0) * BN; *kend = sn;
+    } else if (tt < n012) {
+      *run = 2; *key0 = t0 + (tt - n01) * BN; *kend = e2;
+    } else {
+      *run = 3; *key0 = s3 + (tt - n012) * BN; *kend = p_last + 1;
+    }
+  };
+  // tile tt of K (is_v false) or V into buf, straight to LDS
+  auto load_tile = [&](bool is_v, char* buf, int tt) {
+    int run, key0, kend;
+    tile_run(tt, &run, &key0, &kend);
+    int vo[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int x = min(key0 + ld_row + 16 * u, kend - 1);
+      int o;
+      if (run == 0)
+        o = (a.sum0 + x) * SLOT_BYTES;
+      else if (run == 1)
+        o = static_cast<int>(__umul24(static_cast<uint32_t>(x * (a.k + 1) + a.k - a0), RB));
+      else if (run == 2)
+        o = text_slot(a, x, m) * SLOT_BYTES;
+      else
+        o = static_cast<int>(__umul24(static_cast<uint32_t>(trow(a, x) - a0), RB));
+      vo[u] = o + chunk16;
+    }
+    const bool cache = run == 0 || run == 2;
+    const __amdgpu_buffer_rsrc_t rs = cache ? (is_v ? rc_v : rc_k) : (is_v ? rs_v : rs_k);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(buf + (64 * wave + 256 * u) * 16), 16, vo[u], 0, 0, 0);
+  };
+
+  f32x16_t oacc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) oacc[db][rr] = 0.f;
+  float l_run = 0.f;
+
+  int koff0, voff[2][4];
+  {
+    const int G = lane >> 4, l16 = lane & 15, rr = l16 >> 2, c4 = l16 & 3;
+    koff0 = lds_off(lane & 31, half);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int d = 32 * db + 16 * (G & 1) + 4 * c4;
+      const int row0 = 4 * (G >> 1) + rr;
+      voff[0][db] = lds_off(row0, d >> 3) + 2 * (d & 7);
+      voff[1][db] = lds_off(row0 + 8, d >> 3) + 2 * (d & 7);
+    }
+  }
+  const uint32_t one2 = 0x3f803f80u;
+
+  auto s_tile = [&](const char* kl, f32x16_t* sacc) {
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) sacc[kb2][rr] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        const bf16x8_t kop = *reinterpret_cast<const bf16x8_t*>(kl + (koff0 ^ (ks << 5)) + 32 * ROW_BYTES * kb2);
+        sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[ks], sacc[kb2], 0, 0, 0);
+      }
+  };
+  // visible iff lo <= key <= hi and key < the run's end
+  auto mask_tile = [&](int tt, f32x16_t* sacc) {
+    int run, key0, kend;
+    tile_run(tt, &run, &key0, &kend);
+    const bool is_sum = run < 2;
+    bool full;
+    if (is_sum)
+      full = key0 + BN - 1 <= min(cw0 - a.C - 1, kend - 1);
+    else
+      full = key0 >= tlo_w1 && key0 + BN - 1 <= min(iw0v, kend - 1);
+    if (!full) {
+      const int lo = is_sum ? -1 : tlo;
+      const int hi = min(is_sum ? smax : qi, kend - 1);
+      const int kbase = key0 + 4 * half;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          const int key = kbase + 32 * kb2 + 8 * (rr >> 2) + (rr & 3);
+          sacc[kb2][rr] = (key >= lo && key <= hi) ? sacc[kb2][rr] : kNegInf;
+        }
+    }
+  };
+  auto tile_max = [&](const f32x16_t* sacc) {
+    float t = kNegInf;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) t = fmaxf(t, sacc[kb2][rr]);
+    return fmaxf(t, __shfl_xor(t, 32)) * a.sl;
+  };
+
+  float m_cur = kNegInf, m_nxt = kNegInf;
+  bool grow = false;
+  auto iter = [&](auto cur_c, int tt, f32x16_t* s_cur, f32x16_t* s_nxt) __attribute__((always_inline)) {
+    constexpr int cur = decltype(cur_c)::value;
+    const int last = n_total - 1;
+    const float alpha = m_cur == kNegInf ? 0.f : fast_exp2(m_cur - m_nxt);
+    if (grow) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) oacc[db][rr] *= alpha;
+    }
+    l_run *= alpha;
+    m_cur = m_nxt;
+    // LDS holds K_{tt+1} and V_tt; V_{tt+1} and K_{tt+2} replace V_{tt-1}, K_tt
+    load_tile(true, lds_v[cur ^ 1], tt + 1 < last ? tt + 1 : last);
+    load_tile(false, lds_k[cur], tt + 2 < last ? tt + 2 : last);
+    s_tile(lds_k[cur ^ 1], s_nxt);
+    const float nm = m_cur == kNegInf ? 0.f : -m_cur;
+    u32x4_t pw[4];
+    auto p_half = [&](int kb2) __attribute__((always_inline)) {
+#pragma unroll
+      for (int rr = 0; rr < 16; rr += 2) {
+        const float p0f = fast_exp2(fmaf(s_cur[kb2][rr], a.sl, nm));
+        const float p1f = fast_exp2(fmaf(s_cur[kb2][rr + 1], a.sl, nm));
+        const uint32_t w = pk_bf16(p0f, p1f);
+        pw[2 * kb2 + (rr >> 3)][(rr & 7) >> 1] = w;
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), __builtin_bit_cast(bf16x2_t, one2),
+                                                l_run, false);
+      }
+    };
+    p_half(0);
+    mask_tile(tt + 1, s_nxt);  // past the last tile: everything masked
+    const char* vl = lds_v[cur];
+    p_half(1);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, pw[ks]);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const bf16x4_t lo = lds_read_tr(vl, voff[0][db] + 16 * ROW_BYTES * ks);
+        const bf16x4_t hi = lds_read_tr(vl, voff[1][db] + 16 * ROW_BYTES * ks);
+        const bf16x8_t vop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop, oacc[db], 0, 0, 0);
+      }
+    }
+    const float tmax = tile_max(s_nxt);
+    grow = __any(tmax > m_cur + kLazyRescale);
+    m_nxt = grow ? fmaxf(m_cur, tmax) : m_cur;
+    __syncthreads();
+  };
+
+  f32x16_t sa[2], sb[2];
+  // n_total >= 1: the segment's own text run holds at least the query
+  load_tile(false, lds_k[0], 0);
+  load_tile(true, lds_v[0], 0);
+  load_tile(false, lds_k[1], n_total > 1 ? 1 : 0);
+  __syncthreads();
+  s_tile(lds_k[0], sa);
+  mask_tile(0, sa);
+  m_nxt = tile_max(sa);
+  grow = true;
+  __syncthreads();
+  for (int tt = 0; tt < n_total; tt += 2) {
+    iter(std::integral_constant<int, 0>(), tt, sa, sb);
+    if (tt + 1 < n_total) iter(std::integral_constant<int, 1>(), tt + 1, sb, sa);
+  }
+  const float m_ref = m_cur;
+  if (!wave_active) return;
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (!q_valid) return;
+  const float inv = 1.f / l_tot;
+  bf16_t* op = static_cast<bf16_t*>(p.out) + (qrow * a.hq + h) * D;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const int d = 32 * db + 8 * qq + 4 * half;
+      uint2 w;
+      w.x = pk_bf16(oacc[db][4 * qq + 0] * inv, oacc[db][4 * qq + 1] * inv);
+      w.y = pk_bf16(oacc[db][4 * qq + 2] * inv, oacc[db][4 * qq + 3] * inv);
+      *reinterpret_cast<uint2*>(op + d) = w;
+    }
+  if (p.lse && half == 0) p.lse[static_cast<int64_t>(h) * a.total_rows + qrow] = (m_ref + log2f(l_tot)) * kLn2;
+}
+
+bool prefill_chunk_mfma_supported(const ChunkArgs& a, int32_t dtype) {
+  const int g = a.hq / a.hkv;
+  const int64_t max_len = a.max_rows + a.slots;  // bounds every index the kernel forms
+  return dtype == KSA_DTYPE_BF16 && a.dqk == D && a.dv == D && !a.v_is_k_prefix &&
+         (g == 1 || g == 2 || g % 4 == 0) && a.slots * SLOT_BYTES < (int64_t(1) << 31) &&
+         a.total_rows * a.hkv * D * 2 < (int64_t(1) << 31) && a.total_rows * a.hq * D < (int64_t(1) << 31) &&
+         max_len < (int64_t(1) << 24);
+}
+
+template <int HPW>
+static hipError_t launch_hpw(const ChunkArgs& c, const ChunkPtrs& p, hipStream_t s) {
+  constexpr int PT = 32 * (4 / HPW);
+  CkArgs a;
+  a.batch = c.batch;
+  a.k = c.k;
+  a.C = c.C;
+  a.hq = c.hq;
+  a.hkv = c.hkv;
+  a.g = c.hq / c.hkv;
+  a.n_hg = a.g / HPW;
+  // text tokens of a segment <= its rows; one more tile for the alignment
+  a.n_tiles = static_cast<int32_t>((c.max_rows + PT - 1) / PT + 1);
+  fast_div(static_cast<uint32_t>(a.k), &a.divk_m, &a.divk_l);
+  a.sl = c.scale * kLog2e;
+  a.slots = static_cast<int32_t>(c.slots);
+  a.sum0 = 1 + a.k + a.C * a.k;
+  a.max_rows = static_cast<int32_t>(c.max_rows);
+  a.max_sum_seg = static_cast<int32_t>(c.max_rows / (c.k + 1) + 1);
+  a.total_rows = c.total_rows;
+  const int64_t sum_items = static_cast<int64_t>(a.batch) * a.hkv * a.max_sum_seg;
+  a.n_sum_blocks = static_cast<int32_t>((sum_items + 3) / 4);
+  const int64_t blocks = static_cast<int64_t>(a.batch) * a.hkv * a.n_hg * a.n_tiles + a.n_sum_blocks;
+  hipLaunchKernelGGL(prefill_chunk_d128_kernel<HPW>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, s, a, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_chunk_mfma(const ChunkArgs& a, const ChunkPtrs& p, hipStream_t s) {
+  const int g = a.hq / a.hkv;
+  if (g == 1) return launch_hpw<1>(a, p, s);
+  if (g == 2) return launch_hpw<2>(a, p, s);
+  return launch_hpw<4>(a, p, s);
+}
+
+}  // namespace ksa

@@ -30,7 +30,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(L):
     decl = _declared()
-    assert len(decl) == 16
+    assert len(decl) == 18
     assert sorted(K.EXPORTS) == decl
     for name in decl:
         assert hasattr(L, name), name
@@ -116,6 +116,29 @@ def test_prefill_bwd_arguments(L):
     mla = _params(head_dim_qk=64, head_dim_v=32, v_is_k_prefix=1)
     assert call(mla)[0] == 2
     assert call(p, batch=0, ptrs=(None,) * 9, ws=None, wsb=0)[0] == 0
+
+
+def test_chunk_and_append_rows_arguments(L):
+    p = _params()
+    fake = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    c = K.ksa_cache(16, 16, 16, 10)
+    rc, msg = _status(L, L.ksa_prefill_chunk(ctypes.byref(p), ctypes.byref(c), 2, None, 10, 20, fake, fake, fake,
+                                             fake, None, None))
+    assert rc == 1 and "NULL" in msg
+    rc, _ = _status(L, L.ksa_prefill_chunk(ctypes.byref(p), None, 2, fake, 10, 20, fake, fake, fake, fake, None,
+                                           None))
+    assert rc == 1
+    rc, _ = _status(L, L.ksa_prefill_chunk(ctypes.byref(p), ctypes.byref(c), 2, fake, -1, 20, fake, fake, fake,
+                                           fake, None, None))
+    assert rc == 1
+    assert L.ksa_prefill_chunk(ctypes.byref(p), ctypes.byref(c), 2, fake, 0, 0, None, None, None, None, None,
+                               None) == 0
+    rc, _ = _status(L, L.ksa_cache_append_rows(ctypes.byref(p), ctypes.byref(c), 2, None, 10, fake, fake, None))
+    assert rc == 1
+    nov = K.ksa_cache(16, None, 16, 10)
+    rc, _ = _status(L, L.ksa_cache_append_rows(ctypes.byref(p), ctypes.byref(nov), 2, fake, 10, fake, fake, None))
+    assert rc == 1
+    assert L.ksa_cache_append_rows(ctypes.byref(p), ctypes.byref(c), 0, None, 10, None, None, None) == 0
 
 
 def test_cache_argument_checks(L):
