@@ -217,6 +217,7 @@ def main() -> int:
             raise RuntimeError(f"decode cache error bits {errs}")
     long_runs = [] if args.no_long else prefill_long(ksa, ksa_synth, torch, dev, stream)
     bwd = prefill_backward(ksa, ksa_synth, torch, w, p, qd, kd, vd, stream)
+    chunked = prefill_chunked(ksa, torch, w, p, qd, kd, vd, stream)
     # the report's summary-free baselines on the same inputs (A/B timing)
     modes = []
     for mode, name, W in ((ksa.MODE_SCA, "sliding chunks (no summaries)", 0),
@@ -271,6 +272,7 @@ def main() -> int:
         "prefill_long": long_runs,
         "prefill_baselines": modes,
         "prefill_backward": bwd,
+        "prefill_chunked": chunked,
         "rope": {"value": round(rope_gbps, 1), "unit": "GB/s", "ms": round(seg_ms["rope"], 4)},
         "breakdown_ms": {s: round(v, 4) for s, v in seg_ms.items()},
         "roofline": {"kernel": "prefill_mfma_d128_kernel", "bound": "mfma", "achieved": round(pre_tflops, 2),
@@ -390,6 +392,41 @@ def prefill_backward(ksa, ksa_synth, torch, w, p, qd, kd, vd, stream, reps: int 
     return {"workload": w.name, "ms": round(ms, 4), "tflops": round(tf, 2),
             "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4), "flops": fl,
             "workspace_mb": round(ksa.ksa_prefill_bwd_workspace_bytes(p, w.batch, w.n_text) / 1e6, 1)}
+
+
+def prefill_chunked(ksa, torch, w, p, qd, kd, vd, stream, n_chunks: int = 8, reps: int = 3) -> dict:
+    """The same workload fed in n_chunks segments through the cache: each
+    segment is prefilled against the cache (ksa_prefill_chunk) and then
+    appended (ksa_cache_append_rows); one pass = the whole sequence."""
+    L = ksa.ksa_augmented_len(w.n_text, w.chunk)
+    bounds = [L * i // n_chunks for i in range(n_chunks + 1)]
+    cache = ksa.Cache(p, w.batch, w.n_text // w.chunk + 1, device=qd.device)
+    segs = []
+    for i in range(n_chunks):
+        a, b = bounds[i], bounds[i + 1]
+        segs.append((torch.tensor([0, b - a], dtype=torch.int64, device=qd.device), b - a,
+                     qd[0, a:b].contiguous(), kd[0, a:b].contiguous(), vd[0, a:b].contiguous()))
+    out = torch.empty((max(s[1] for s in segs), w.hq, w.dv), dtype=w.dtype, device=qd.device)
+
+    def one_pass():
+        ksa.ksa_cache_reset(cache, stream=stream)
+        for seg, rows, q_, k_, v_ in segs:
+            ksa.ksa_prefill_chunk(cache, seg, rows, q_, k_, v_, out=out[:rows], stream=stream)
+            ksa.ksa_cache_append_rows(cache, seg, rows, k_, v_, stream=stream)
+
+    one_pass()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(reps):
+        one_pass()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / reps
+    fl = 2 * (w.dqk + w.dv) * w.hq * visible_pairs(w.n_text, w.chunk, w.window) * w.batch
+    del cache, segs, out
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "segments": n_chunks, "ms": round(ms, 4),
+            "tflops": round(fl / (ms * 1e-3) / 1e12, 2)}
 
 
 def cpu_baseline(w, rows_req: int) -> dict:

@@ -21,6 +21,7 @@ SOURCES = [
     "ksa_prefill_bwd_mfma.hip",
     "ksa_prefill_chunk_generic.hip",
     "ksa_prefill_chunk_mfma.hip",
+    "ksa_prefill_mla.hip",
     "ksa_cache.hip",
     "ksa_decode.hip",
     "ksa_decode_mla.hip",

@@ -209,6 +209,8 @@ int32_t ksa_prefill_attn_mode(const ksa_params* p, int32_t mode, int64_t window_
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (ksa::prefill_mfma_supported(a, p->dtype))
     return hip_status(ksa::launch_prefill_mfma_d128(a, q, k, v, out, lse, s), "prefill");
+  if (ksa::prefill_mla_supported(a, p->dtype))
+    return hip_status(ksa::launch_prefill_mla(a, k, q, out, lse, s), "prefill");
   return hip_status(ksa::launch_prefill_generic(a, p->dtype, 0, q, k, v, out, lse, s), "prefill");
 }
 

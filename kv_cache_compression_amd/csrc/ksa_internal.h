@@ -40,6 +40,10 @@ hipError_t launch_prefill_generic(const PrefillArgs& a, int32_t dtype, int rows_
 hipError_t launch_prefill_mfma_d128(const PrefillArgs& a, const void* q, const void* k,
                                     const void* v, void* out, float* lse, hipStream_t s);
 bool prefill_mfma_supported(const PrefillArgs& a, int32_t dtype);
+// bf16 absorbed-MLA prefill: Hq = 128, Hkv = 1, Dqk = 576, Dv = 512 (V = K prefix).
+bool prefill_mla_supported(const PrefillArgs& a, int32_t dtype);
+hipError_t launch_prefill_mla(const PrefillArgs& a, const void* k, const void* q, void* out, float* lse,
+                              hipStream_t s);
 
 // Backward of the prefill.  delta[b, h, row] = dot(dout, out) in fp32.
 hipError_t launch_bwd_delta(const PrefillArgs& a, int32_t dtype, const void* out, const void* dout,
