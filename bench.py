@@ -218,6 +218,7 @@ def main() -> int:
     long_runs = [] if args.no_long else prefill_long(ksa, ksa_synth, torch, dev, stream)
     bwd = prefill_backward(ksa, ksa_synth, torch, w, p, qd, kd, vd, stream)
     chunked = prefill_chunked(ksa, torch, w, p, qd, kd, vd, stream)
+    mla_pre = prefill_mla(ksa, ksa_synth, torch, dev, stream)
     # the report's summary-free baselines on the same inputs (A/B timing)
     modes = []
     for mode, name, W in ((ksa.MODE_SCA, "sliding chunks (no summaries)", 0),
@@ -273,6 +274,7 @@ def main() -> int:
         "prefill_baselines": modes,
         "prefill_backward": bwd,
         "prefill_chunked": chunked,
+        "prefill_mla": mla_pre,
         "rope": {"value": round(rope_gbps, 1), "unit": "GB/s", "ms": round(seg_ms["rope"], 4)},
         "breakdown_ms": {s: round(v, 4) for s, v in seg_ms.items()},
         "roofline": {"kernel": "prefill_mfma_d128_kernel", "bound": "mfma", "achieved": round(pre_tflops, 2),
@@ -427,6 +429,31 @@ def prefill_chunked(ksa, torch, w, p, qd, kd, vd, stream, n_chunks: int = 8, rep
     torch.cuda.empty_cache()
     return {"workload": w.name, "segments": n_chunks, "ms": round(ms, 4),
             "tflops": round(fl / (ms * 1e-3) / 1e12, 2)}
+
+
+def prefill_mla(ksa, ksa_synth, torch, dev, stream, reps: int = 5) -> dict:
+    """Absorbed-MLA prefill: 128 heads over one 576/512 latent head."""
+    w = ksa_synth.PREFILL_MLA_8K
+    L = ksa.ksa_augmented_len(w.n_text, w.chunk)
+    g = ksa_synth.gen(w.seed)
+    qd = ksa_synth.normal((w.batch, L, w.hq, w.dqk), w.dtype, g).to(dev)
+    kd = ksa_synth.normal((w.batch, L, w.hkv, w.dqk), w.dtype, g).to(dev)
+    p = ksa.Params(w.chunk, w.window, w.hq, w.hkv, w.dqk, w.dv, w.dtype, v_is_k_prefix=True)
+    out = torch.empty((w.batch, L, w.hq, w.dv), dtype=w.dtype, device=dev)
+    ksa.ksa_prefill_attn(p, qd, kd, None, w.n_text, out=out, stream=stream)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(reps):
+        ksa.ksa_prefill_attn(p, qd, kd, None, w.n_text, out=out, stream=stream)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / reps
+    fl = 2 * (w.dqk + w.dv) * w.hq * visible_pairs(w.n_text, w.chunk, w.window) * w.batch
+    tf = fl / (ms * 1e-3) / 1e12
+    del qd, kd, out
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "ms": round(ms, 4), "tflops": round(tf, 2),
+            "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4), "flops": fl}
 
 
 def cpu_baseline(w, rows_req: int) -> dict:

@@ -62,6 +62,9 @@ PREFILL_128K_W16 = PrefillWorkload("prefill_n131072_k8_w16_h32x8_d128_bf16", 1, 
                                    128, 128, torch.bfloat16, 1e6, 2)
 DECODE_GQA = DecodeWorkload("decode_b64_n131072_k8_w64_h32x8_d128_bf16", 64, 8, 64, 32, 8, 128, 128,
                             False, torch.bfloat16, 3, fixed_chunks=16384)
+# absorbed-MLA prefill: 128 query heads over one 576/512 latent head (V = K prefix)
+PREFILL_MLA_8K = PrefillWorkload("prefill_mla_n8192_k8_w64_h128x1_d576x512_bf16", 1, 8192, 8, 64, 128, 1, 576, 512,
+                                 torch.bfloat16, 1e6, 5)
 DECODE_MLA = DecodeWorkload("decode_mla_b32_n16k-128k_k8_w64_h128x1_d576x512_bf16", 32, 8, 64, 128, 1,
                             576, 512, True, torch.bfloat16, 4, ragged_lo=16384, ragged_hi=131072)
 
