@@ -83,6 +83,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-long", action="store_true", help="skip the 131072-token prefill lines")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the backward, chunked, MLA-prefill and baseline-mode lines")
     ap.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0 = auto)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 256 MiB device copy three times (counter calibration)")
@@ -216,24 +218,10 @@ def main() -> int:
         if any(errs):
             raise RuntimeError(f"decode cache error bits {errs}")
     long_runs = [] if args.no_long else prefill_long(ksa, ksa_synth, torch, dev, stream)
-    bwd = prefill_backward(ksa, ksa_synth, torch, w, p, qd, kd, vd, stream)
-    chunked = prefill_chunked(ksa, torch, w, p, qd, kd, vd, stream)
-    mla_pre = prefill_mla(ksa, ksa_synth, torch, dev, stream)
-    # the report's summary-free baselines on the same inputs (A/B timing)
-    modes = []
-    for mode, name, W in ((ksa.MODE_SCA, "sliding chunks (no summaries)", 0),
-                          (ksa.MODE_SWA, f"token window of {w.window * w.chunk}", w.window * w.chunk)):
-        ksa.ksa_prefill_attn_mode(p, mode, W, qd, kd, vd, w.n_text, out=out, stream=stream)
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        ev[0].record(stream)
-        for _ in range(5):
-            ksa.ksa_prefill_attn_mode(p, mode, W, qd, kd, vd, w.n_text, out=out, stream=stream)
-        ev[1].record(stream)
-        torch.cuda.synchronize()
-        ms = ev[0].elapsed_time(ev[1]) / 5
-        fl = 2 * (w.dqk + w.dv) * w.hq * baseline_pairs(w.n_text, w.chunk, mode, w.window, W) * w.batch
-        modes.append({"mode": name, "ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
-                      "ksa_ms": round(seg_ms["prefill"], 4)})
+    bwd, chunked, mla_pre, modes = None, None, None, []
+    if not args.no_extra:
+        bwd, chunked, mla_pre, modes = extra_lines(ksa, ksa_synth, torch, dev, stream, w, p, qd, kd, vd, out,
+                                                   seg_ms["prefill"])
 
     pre_tflops = flops / (seg_ms["prefill"] * 1e-3) / 1e12
     dec_gbps = dec_bytes / (seg_ms["decode"] * 1e-3) / 1e9
@@ -364,6 +352,29 @@ def prefill_long(ksa, ksa_synth, torch, dev, stream, reps: int = 5) -> list:
         del qd, kd, vd, out
         torch.cuda.empty_cache()
     return res
+
+
+def extra_lines(ksa, ksa_synth, torch, dev, stream, w, p, qd, kd, vd, out, ksa_ms):
+    """The backward, the chunked prefill, the MLA prefill and the report's
+    summary-free baselines on the same inputs (A/B timing)."""
+    bwd = prefill_backward(ksa, ksa_synth, torch, w, p, qd, kd, vd, stream)
+    chunked = prefill_chunked(ksa, torch, w, p, qd, kd, vd, stream)
+    mla_pre = prefill_mla(ksa, ksa_synth, torch, dev, stream)
+    modes = []
+    for mode, name, W in ((ksa.MODE_SCA, "sliding chunks (no summaries)", 0),
+                          (ksa.MODE_SWA, f"token window of {w.window * w.chunk}", w.window * w.chunk)):
+        ksa.ksa_prefill_attn_mode(p, mode, W, qd, kd, vd, w.n_text, out=out, stream=stream)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(5):
+            ksa.ksa_prefill_attn_mode(p, mode, W, qd, kd, vd, w.n_text, out=out, stream=stream)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / 5
+        fl = 2 * (w.dqk + w.dv) * w.hq * baseline_pairs(w.n_text, w.chunk, mode, w.window, W) * w.batch
+        modes.append({"mode": name, "ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+                      "ksa_ms": round(ksa_ms, 4)})
+    return bwd, chunked, mla_pre, modes
 
 
 def prefill_backward(ksa, ksa_synth, torch, w, p, qd, kd, vd, stream, reps: int = 5) -> dict:
