@@ -17,11 +17,16 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 
-// 16-byte chunk c (0..15) of LDS row `row` is stored at chunk c ^ swz(row):
-// 8 consecutive rows hit 8 different even chunks and the next 8 the odd
-// ones, so MFMA operand reads (32 rows x 16 B) and transposing reads
-// (4 rows x 32 B per 16 lanes) spread over the banks.
-__device__ __forceinline__ int lds_swz(int row) { return ((row & 7) << 1) | ((row >> 3) & 1); }
+// 16-byte chunk c (0..15) of LDS row `row` is stored at chunk c ^ swz(row),
+// swz(row) = 4 (row % 4) + (row / 4) % 4, a bijection on 16 consecutive rows:
+//   - MFMA operand reads (16 lanes = 16 rows, one logical chunk) land on 16
+//     different chunk positions, i.e. all 64 banks once;
+//   - transposing reads (per 32 lanes: 4 rows x 4 consecutive chunks
+//     4q .. 4q+3) flip the chunk's two upper bits by row % 4, so the 16
+//     (row, chunk) pairs also take 16 different positions.
+// The DMA writes stay linear (lane l writes bytes 16 l ..): the global side
+// fetches the chunk that belongs there.
+__device__ __forceinline__ int lds_swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 __device__ __forceinline__ int lds_off(int row, int chunk) {
   return row * ROW_BYTES + ((chunk ^ lds_swz(row)) << 4);
 }

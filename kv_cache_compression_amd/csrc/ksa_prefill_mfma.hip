@@ -245,7 +245,7 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_d128_kernel(
   // direct-to-LDS loads place lane chunks linearly (row tid/16 + 16 u,
   // physical chunk tid % 16); the thread loads the logical chunk that the
   // swizzle maps there
-  const int chunk16 = 16 * (ld_chunk ^ (((ld_row & 7) << 1) | ((ld_row >> 3) & 1)));
+  const int chunk16 = 16 * (ld_chunk ^ lds_swz(ld_row));
   const int sum_step = (a.k + 1) * RB;  // bytes between consecutive summary rows
   const int s_c0 = ld_row * sum_step + a.k * RB + chunk16;
   const int s_lim = (sn > 0 ? (sn - 1) * sum_step + a.k * RB : 0) + chunk16;
