@@ -229,9 +229,9 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_d128_kernel(
       qop[ks] = q_valid ? *reinterpret_cast<const bf16x8_t*>(qp + 16 * ks) : bf16x8_t{};
   }
 
-  // Global -> register prefetch: thread owns 16-byte chunk (tid % 16) of
-  // rows tid/16 + 16 u of a tile.  Tile indices are clamped to the last
-  // tile, so loads are always in range and the loop body has no branches.
+  // Tile loads: thread owns 16-byte chunk (tid % 16) of rows tid/16 + 16 u
+  // of a tile.  Tile indices are clamped to the last tile, so the loop body
+  // loads without branching on the tile count.
   const int ld_chunk = tid & 15;
   const int ld_row = tid >> 4;
   const int kvs = a.hkv * D;  // elements per augmented row
@@ -248,26 +248,36 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_d128_kernel(
   const int chunk16 = 16 * (ld_chunk ^ lds_swz(ld_row));
   const int sum_step = (a.k + 1) * RB;  // bytes between consecutive summary rows
   const int s_c0 = ld_row * sum_step + a.k * RB + chunk16;
-  const int s_lim = (sn > 0 ? (sn - 1) * sum_step + a.k * RB : 0) + chunk16;
   __shared__ __attribute__((aligned(16))) char lds_k0[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char lds_k1[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char lds_v0[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char lds_v1[TILE_BYTES];
   char* const lds_k[2] = {lds_k0, lds_k1};
   char* const lds_v[2] = {lds_v0, lds_v1};
-  // byte offsets of this thread's 4 rows of tile tt
+  // byte offsets of this thread's 4 rows of tile tt.  Rows past a run's end
+  // are read (masked later) or, past the sequence, return zeros through the
+  // buffer range check.  When k divides 64 a text tile starts 64 + 64/k rows
+  // after the previous one.
+  int t_base[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    t_base[u] = static_cast<int>(__umul24(static_cast<uint32_t>(trow(a, t0 + ld_row + 16 * u)), RB)) + chunk16;
+  const int t_step = (BN + BN / a.k) * RB;
+  const bool k_div = (BN % a.k) == 0;
   auto tile_offsets = [&](int tt, int* vo) {
     if (tt < ns) {
       const int sb = s_c0 + tt * BN * sum_step;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) vo[u] = min(sb + 16 * u * sum_step, s_lim);
+      for (int u = 0; u < 4; ++u) vo[u] = sb + 16 * u * sum_step;
+    } else if (k_div) {
+      const int d = (tt - ns) * t_step;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) vo[u] = t_base[u] + d;
     } else {
       const int x0 = t0 + (tt - ns) * BN + ld_row;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int x = min(x0 + 16 * u, p_last);
-        vo[u] = static_cast<int>(__umul24(static_cast<uint32_t>(trow(a, x)), RB)) + chunk16;
-      }
+      for (int u = 0; u < 4; ++u)
+        vo[u] = static_cast<int>(__umul24(static_cast<uint32_t>(trow(a, x0 + 16 * u)), RB)) + chunk16;
     }
   };
   auto load_tile = [&](const __amdgpu_buffer_rsrc_t& rs, char* buf, int tt) {
@@ -334,12 +344,14 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_d128_kernel(
       const int lo = is_sum ? -1 : tlo;
       const int hi = is_sum ? smax : thi;
       const int kbase = key0 + 4 * half;
+      // key offsets 32 kb2 + 8 (r / 4) + r % 4 against per-lane bounds
+      const int lo_r = lo - kbase, hi_r = hi - kbase;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = kbase + 32 * kb2 + 8 * (r >> 2) + (r & 3);
-          sacc[kb2][r] = (key >= lo && key <= hi) ? sacc[kb2][r] : kNegInf;
+          const int off = 32 * kb2 + 8 * (r >> 2) + (r & 3);
+          sacc[kb2][r] = (off >= lo_r && off <= hi_r) ? sacc[kb2][r] : kNegInf;
         }
     }
   };
