@@ -230,26 +230,35 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_d128_kernel(
   const int chunk16 = 16 * (ld_chunk ^ lds_swz(ld_row));
   const int sum_step = (a.k + 1) * RB;
   const int s_c0 = ld_row * sum_step + a.k * RB + chunk16;
-  const int s_lim = (sn > 0 ? (sn - 1) * sum_step + a.k * RB : 0) + chunk16;
   __shared__ __attribute__((aligned(16))) char lds_k0[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char lds_k1[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char lds_v0[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char lds_v1[TILE_BYTES];
   char* const lds_k[2] = {lds_k0, lds_k1};
   char* const lds_v[2] = {lds_v0, lds_v1};
+  // rows past a run's end are masked or, past the sequence, read as zeros;
+  // when k divides 64 a text tile starts 64 + 64/k rows after the previous
+  int t_base[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    t_base[u] = static_cast<int>(__umul24(static_cast<uint32_t>(trow(a, t0 + ld_row + 16 * u)), RB)) + chunk16;
+  const int t_step = (BN + BN / a.k) * RB;
+  const bool k_div = (BN % a.k) == 0;
   auto load_tile = [&](const __amdgpu_buffer_rsrc_t& rs, char* buf, int tt) {
     int vo[4];
     if (tt < ns) {
       const int sb = s_c0 + tt * BN * sum_step;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) vo[u] = min(sb + 16 * u * sum_step, s_lim);
+      for (int u = 0; u < 4; ++u) vo[u] = sb + 16 * u * sum_step;
+    } else if (k_div) {
+      const int d = (tt - ns) * t_step;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) vo[u] = t_base[u] + d;
     } else {
       const int x0 = t0 + (tt - ns) * BN + ld_row;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int x = min(x0 + 16 * u, p_last);
-        vo[u] = static_cast<int>(__umul24(static_cast<uint32_t>(trow(a, x)), RB)) + chunk16;
-      }
+      for (int u = 0; u < 4; ++u)
+        vo[u] = static_cast<int>(__umul24(static_cast<uint32_t>(trow(a, x0 + 16 * u)), RB)) + chunk16;
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u)
@@ -307,15 +316,14 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_d128_kernel(
     const int key0 = is_sum ? tt * BN : t0 + (tt - ns) * BN;
     const bool full = is_sum ? key0 + BN - 1 <= cw0 - a.C - 1 : (key0 >= tlo_w1 && key0 + BN - 1 <= iw0);
     if (!full) {
-      const int lo = is_sum ? -1 : tlo;
-      const int hi = is_sum ? smax : qi;
       const int kbase = key0 + 4 * half;
+      const int lo_r = (is_sum ? -1 : tlo) - kbase, hi_r = (is_sum ? smax : qi) - kbase;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = kbase + 32 * kb2 + 8 * (r >> 2) + (r & 3);
-          s[kb2][r] = (key >= lo && key <= hi) ? s[kb2][r] : kNegInf;
+          const int off = 32 * kb2 + 8 * (r >> 2) + (r & 3);
+          s[kb2][r] = (off >= lo_r && off <= hi_r) ? s[kb2][r] : kNegInf;
         }
     }
     // dS^T packed as the B operand of dQ^T += K^T dS^T (keys 16 ks + ...)
