@@ -176,17 +176,43 @@ __global__ void __launch_bounds__(256) decode_gqa_d128_split_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
 
-  for (int64_t t0 = r0 + static_cast<int64_t>(wave) * kDecTile; t0 < r1;
-       t0 += kDecWaves * kDecTile) {
+  // K and V rows of the next tile are loaded while the current one is used
+  // (rows clamped into the range; a clamped row gets weight 0).
+  const int64_t stride = kDecWaves * kDecTile;
+  auto load_k = [&](int64_t t, bf16x8_t* kop) {
+    const int64_t kr = t + col < r1 ? t + col : r1 - 1;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) kop[ks] = *reinterpret_cast<const bf16x8_t*>(kc + kr * D + 32 * ks + 8 * grp);
+  };
+  auto load_v = [&](int64_t t, uint4* vr) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t row = t + grp + 4 * i;
+      vr[i] = *reinterpret_cast<const uint4*>(vc + (row < r1 ? row : r1 - 1) * D + 8 * col);
+    }
+  };
+  int64_t t0 = r0 + static_cast<int64_t>(wave) * kDecTile;
+  bf16x8_t kop_n[4];
+  uint4 v_n[4];
+  if (t0 < r1) {
+    load_k(t0, kop_n);
+    load_v(t0, v_n);
+  }
+  for (; t0 < r1; t0 += stride) {
+    bf16x8_t kop[4];
+    uint4 vr[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) kop[ks] = kop_n[ks];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vr[i] = v_n[i];
+    if (t0 + stride < r1) {
+      load_k(t0 + stride, kop_n);
+      load_v(t0 + stride, v_n);
+    }
     // ---- S = K Q^T for 16 rows (MFMA, A = K rows) ----
-    const int64_t krow_raw = t0 + col;
-    const int64_t krow = krow_raw < r1 ? krow_raw : r1 - 1;
     f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8_t kop = *reinterpret_cast<const bf16x8_t*>(kc + krow * D + 32 * ks + 8 * grp);
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[ks], s, 0, 0, 0);
-    }
+    for (int ks = 0; ks < 4; ++ks) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[ks], qop[ks], s, 0, 0, 0);
     // C layout: lane holds head `col`, rows 4 grp + i.
     float sv[4];
     float tmax = kNegInf;
@@ -225,24 +251,21 @@ __global__ void __launch_bounds__(256) decode_gqa_d128_split_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int rl = grp + 4 * i;
-      const int64_t row = t0 + rl;
-      if (row < r1) {
-        const uint4 vraw = *reinterpret_cast<const uint4*>(vc + row * D + 8 * col);
-        float vv[8];
-        vv[0] = __uint_as_float(vraw.x << 16);
-        vv[1] = __uint_as_float(vraw.x & 0xffff0000u);
-        vv[2] = __uint_as_float(vraw.y << 16);
-        vv[3] = __uint_as_float(vraw.y & 0xffff0000u);
-        vv[4] = __uint_as_float(vraw.z << 16);
-        vv[5] = __uint_as_float(vraw.z & 0xffff0000u);
-        vv[6] = __uint_as_float(vraw.w << 16);
-        vv[7] = __uint_as_float(vraw.w & 0xffff0000u);
+      const uint4 vraw = vr[i];
+      float vv[8];
+      vv[0] = __uint_as_float(vraw.x << 16);
+      vv[1] = __uint_as_float(vraw.x & 0xffff0000u);
+      vv[2] = __uint_as_float(vraw.y << 16);
+      vv[3] = __uint_as_float(vraw.y & 0xffff0000u);
+      vv[4] = __uint_as_float(vraw.z << 16);
+      vv[5] = __uint_as_float(vraw.z & 0xffff0000u);
+      vv[6] = __uint_as_float(vraw.w << 16);
+      vv[7] = __uint_as_float(vraw.w & 0xffff0000u);
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float p = p_lds[wave][rl][h];
+      for (int h = 0; h < G; ++h) {
+        const float p = p_lds[wave][rl][h];  // 0 for rows past the range
 #pragma unroll
-          for (int e = 0; e < 8; ++e) o[h][e] += p * vv[e];
-        }
+        for (int e = 0; e < 8; ++e) o[h][e] += p * vv[e];
       }
     }
     __builtin_amdgcn_wave_barrier();  // p_lds reuse in the next tile
