@@ -229,7 +229,8 @@ KSA_API int32_t ksa_cache_append_rows(const ksa_params* p, const ksa_cache* c, i
  *   out [total_rows, Hq, Dv]    lse [Hq, total_rows] fp32 natural log, or NULL
  *   max_rows >= every R_b, total_rows = seg_rows[batch].
  * The cache is read only; ksa_cache_append_rows with the same seg_rows and
- * k / v then moves the segment into it. */
+ * k / v then moves the segment into it.  A sequence whose cache state is out
+ * of range (m > max_summaries, r > k) is skipped: its rows are not written. */
 KSA_API int32_t ksa_prefill_chunk(const ksa_params* p, const ksa_cache* c, int32_t batch,
                           const int64_t* seg_rows, int64_t max_rows, int64_t total_rows, const void* q,
                           const void* k, const void* v, void* out, float* lse, void* stream);

@@ -67,6 +67,7 @@ __device__ void chunk_summary_wave(const CkArgs& a, int64_t item, const ChunkPtr
   const int kvh = static_cast<int>((item / a.max_sum_seg) % a.hkv);
   const int b = static_cast<int>(item / (static_cast<int64_t>(a.max_sum_seg) * a.hkv));
   const int m = p.state[4 * b], r = p.state[4 * b + 1];
+  if (m < 0 || m > a.slots - a.sum0 || r < 0 || r > a.k) return;  // state out of range: skipped
   const int64_t off = p.seg_rows[b];
   const int a0 = m * (a.k + 1) + r;
   const int a1 = a0 + static_cast<int>(p.seg_rows[b + 1] - off);
@@ -159,6 +160,7 @@ __global__ void __launch_bounds__(256, 2) prefill_chunk_d128_kernel(CkArgs a, Ch
 
   const int m = __builtin_amdgcn_readfirstlane(p.state[4 * b]);
   const int r = __builtin_amdgcn_readfirstlane(p.state[4 * b + 1]);
+  if (m < 0 || m > a.slots - a.sum0 || r < 0 || r > a.k) return;  // state out of range: skipped
   const int64_t off = p.seg_rows[b];
   const int R = static_cast<int>(p.seg_rows[b + 1] - off);
   const int a0 = m * (a.k + 1) + r, a1 = a0 + R;

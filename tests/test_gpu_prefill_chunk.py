@@ -166,3 +166,27 @@ def test_chunked_prefill_long_history():
     n, k, C = 3000, 8, 8
     L = O.augmented_len(n, k)
     _chunk_case(torch.bfloat16, 128, n, k, C, 8, 2, [[L - 150, 150], [L - 1, 1]], seed=99)
+
+
+@pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 128), (torch.float32, 32)])
+def test_chunk_skips_sequences_with_bad_state(dtype, D):
+    """A cache state out of range (m beyond the summary capacity, r > k)
+    leaves that sequence's rows unwritten; the other sequence is computed."""
+    dev = _dev()
+    k, C, n = 8, 2, 40
+    L = O.augmented_len(n, k)
+    p = ksa.Params(k, C, 4, 2, D, D, dtype)
+    cache = ksa.Cache(p, 2, 8, device=dev)
+    g = ksa_synth.gen(3)
+    q = ksa_synth.normal((2 * L, 4, D), dtype, g).to(dev)
+    kx = ksa_synth.normal((2 * L, 2, D), dtype, g).to(dev)
+    v = ksa_synth.normal((2 * L, 2, D), dtype, g).to(dev)
+    seg = torch.tensor([0, L, 2 * L], dtype=torch.int64, device=dev)
+    for bad in ([9, 0], [0, k + 1], [-1, 0]):
+        cache.state.zero_()
+        cache.state[1, :2] = torch.tensor(bad, dtype=torch.int32)
+        out = torch.full((2 * L, 4, D), float("nan"), dtype=dtype, device=dev)
+        ksa.ksa_prefill_chunk(cache, seg, L, q, kx, v, out=out)
+        torch.cuda.synchronize()
+        assert torch.isnan(out[L:].float()).all(), bad
+        assert not torch.isnan(out[:L].float()).any(), bad
