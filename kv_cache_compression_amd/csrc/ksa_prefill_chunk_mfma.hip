@@ -226,22 +226,27 @@ __global__ void __launch_bounds__(256, 2) prefill_chunk_d128_kernel(CkArgs a, Ch
   __shared__ __attribute__((aligned(16))) char lds_v1[TILE_BYTES];
   char* const lds_k[2] = {lds_k0, lds_k1};
   char* const lds_v[2] = {lds_v0, lds_v1};
-  // tile tt -> run (0..3), first key, run end (exclusive)
-  auto tile_run = [&](int tt, int* run, int* key0, int* kend) {
-    if (tt < n0) {
-      *run = 0; *key0 = tt * BN; *kend = e0;
-    } else if (tt < n01) {
-      *run = 1; *key0 = m + (tt - n0) * BN; *kend = sn;
-    } else if (tt < n012) {
-      *run = 2; *key0 = t0 + (tt - n01) * BN; *kend = e2;
-    } else {
-      *run = 3; *key0 = s3 + (tt - n012) * BN; *kend = p_last + 1;
-    }
-  };
-  // tile tt of K (is_v false) or V into buf, straight to LDS
-  auto load_tile = [&](bool is_v, char* buf, int tt) {
+  // tile tt -> run (0..3), first key, run end (exclusive); computed once per
+  // tile and carried through the pipeline
+  struct TileDesc {
     int run, key0, kend;
-    tile_run(tt, &run, &key0, &kend);
+  };
+  auto tile_run = [&](int tt) {
+    TileDesc d;
+    if (tt < n0) {
+      d.run = 0; d.key0 = tt * BN; d.kend = e0;
+    } else if (tt < n01) {
+      d.run = 1; d.key0 = m + (tt - n0) * BN; d.kend = sn;
+    } else if (tt < n012) {
+      d.run = 2; d.key0 = t0 + (tt - n01) * BN; d.kend = e2;
+    } else {
+      d.run = 3; d.key0 = s3 + (tt - n012) * BN; d.kend = p_last + 1;
+    }
+    return d;
+  };
+  // a tile of K (is_v false) or V into buf, straight to LDS
+  auto load_tile = [&](bool is_v, char* buf, const TileDesc& d) {
+    const int run = d.run, key0 = d.key0, kend = d.kend;
     int vo[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -300,9 +305,8 @@ __global__ void __launch_bounds__(256, 2) prefill_chunk_d128_kernel(CkArgs a, Ch
       }
   };
   // visible iff lo <= key <= hi and key < the run's end
-  auto mask_tile = [&](int tt, f32x16_t* sacc) {
-    int run, key0, kend;
-    tile_run(tt, &run, &key0, &kend);
+  auto mask_tile = [&](const TileDesc& d, f32x16_t* sacc) {
+    const int run = d.run, key0 = d.key0, kend = d.kend;
     const bool is_sum = run < 2;
     bool full;
     if (is_sum)
@@ -333,6 +337,7 @@ __global__ void __launch_bounds__(256, 2) prefill_chunk_d128_kernel(CkArgs a, Ch
 
   float m_cur = kNegInf, m_nxt = kNegInf;
   bool grow = false;
+  TileDesc d1;  // tile tt + 1 (clamped to the last), carried between iterations
   auto iter = [&](auto cur_c, int tt, f32x16_t* s_cur, f32x16_t* s_nxt) __attribute__((always_inline)) {
     constexpr int cur = decltype(cur_c)::value;
     const int last = n_total - 1;
@@ -346,8 +351,9 @@ __global__ void __launch_bounds__(256, 2) prefill_chunk_d128_kernel(CkArgs a, Ch
     l_run *= alpha;
     m_cur = m_nxt;
     // LDS holds K_{tt+1} and V_tt; V_{tt+1} and K_{tt+2} replace V_{tt-1}, K_tt
-    load_tile(true, lds_v[cur ^ 1], tt + 1 < last ? tt + 1 : last);
-    load_tile(false, lds_k[cur], tt + 2 < last ? tt + 2 : last);
+    const TileDesc d2 = tile_run(tt + 2 < last ? tt + 2 : last);
+    load_tile(true, lds_v[cur ^ 1], d1);
+    load_tile(false, lds_k[cur], d2);
     s_tile(lds_k[cur ^ 1], s_nxt);
     const float nm = m_cur == kNegInf ? 0.f : -m_cur;
     u32x4_t pw[4];
@@ -363,7 +369,7 @@ __global__ void __launch_bounds__(256, 2) prefill_chunk_d128_kernel(CkArgs a, Ch
       }
     };
     p_half(0);
-    mask_tile(tt + 1, s_nxt);  // past the last tile: everything masked
+    mask_tile(d1, s_nxt);  // past the last tile S is never used
     const char* vl = lds_v[cur];
     p_half(1);
 #pragma unroll
@@ -380,17 +386,22 @@ __global__ void __launch_bounds__(256, 2) prefill_chunk_d128_kernel(CkArgs a, Ch
     const float tmax = tile_max(s_nxt);
     grow = __any(tmax > m_cur + kLazyRescale);
     m_nxt = grow ? fmaxf(m_cur, tmax) : m_cur;
+    d1 = d2;
     __syncthreads();
   };
 
   f32x16_t sa[2], sb[2];
   // n_total >= 1: the segment's own text run holds at least the query
-  load_tile(false, lds_k[0], 0);
-  load_tile(true, lds_v[0], 0);
-  load_tile(false, lds_k[1], n_total > 1 ? 1 : 0);
-  __syncthreads();
-  s_tile(lds_k[0], sa);
-  mask_tile(0, sa);
+  {
+    const TileDesc d0 = tile_run(0);
+    d1 = tile_run(n_total > 1 ? 1 : 0);
+    load_tile(false, lds_k[0], d0);
+    load_tile(true, lds_v[0], d0);
+    load_tile(false, lds_k[1], d1);
+    __syncthreads();
+    s_tile(lds_k[0], sa);
+    mask_tile(d0, sa);
+  }
   m_nxt = tile_max(sa);
   grow = true;
   __syncthreads();
