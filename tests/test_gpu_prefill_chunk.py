@@ -190,3 +190,29 @@ def test_chunk_skips_sequences_with_bad_state(dtype, D):
         torch.cuda.synchronize()
         assert torch.isnan(out[L:].float()).all(), bad
         assert not torch.isnan(out[:L].float()).any(), bad
+
+
+def test_chunked_prefill_absorbed_latent_generic():
+    """V as the first Dv columns of K (absorbed latent form), fp32 generic path:
+    chunked prefill through the cache equals the one-shot oracle."""
+    dev = _dev()
+    n, k, C, hq, dqk, dv = 150, 4, 3, 4, 48, 32
+    L = O.augmented_len(n, k)
+    g = ksa_synth.gen(31)
+    q = ksa_synth.normal((L, hq, dqk), torch.float32, g)
+    kx = ksa_synth.normal((L, 1, dqk), torch.float32, g)
+    p = ksa.Params(k, C, hq, 1, dqk, dv, torch.float32, v_is_k_prefix=True)
+    ref, rl = O.ksa_attention(q.double().numpy(), kx.double().numpy(), None, n, k, C, p.scale, dv=dv)
+    cache = ksa.Cache(p, 1, n // k + 1, device=dev)
+    start = 0
+    for cnt in (7, 1, k, 40, L - 52):
+        seg = torch.tensor([0, cnt], dtype=torch.int64, device=dev)
+        qs, ks_ = q[start:start + cnt].to(dev), kx[start:start + cnt].to(dev)
+        lse = torch.empty((hq, cnt), dtype=torch.float32, device=dev)
+        out = ksa.ksa_prefill_chunk(cache, seg, cnt, qs, ks_, None, lse=lse)
+        ksa.ksa_cache_append_rows(cache, seg, cnt, ks_, None)
+        torch.cuda.synchronize()
+        assert np.abs(_np(out) - ref[start:start + cnt]).max() <= 1e-4
+        assert np.abs(_np(lse) - rl[:, start:start + cnt]).max() <= 1e-4
+        start += cnt
+    assert cache.state[0, 0].item() == n // k and cache.state[0, 1].item() == n % k
