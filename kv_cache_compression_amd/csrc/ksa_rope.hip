@@ -77,10 +77,11 @@ __global__ void __launch_bounds__(256) rope_bf16x8_kernel(RopeArgs a, bf16_t* __
     inv_freq *= ratio;
   }
   bf16_t* base = x + br * a.heads * static_cast<int64_t>(a.head_dim) + a.rot_off + f0;
+#pragma unroll 4
   for (int32_t h = 0; h < a.heads; ++h) {
     bf16_t* p = base + static_cast<int64_t>(h) * a.head_dim;
-    const u32x4 lo = *reinterpret_cast<const u32x4*>(p);
-    const u32x4 hi = *reinterpret_cast<const u32x4*>(p + half);
+    const u32x4 lo = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    const u32x4 hi = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + half));
     u32x4 olo, ohi;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
