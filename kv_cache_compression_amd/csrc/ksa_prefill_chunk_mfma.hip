@@ -19,8 +19,8 @@
 // loads stay direct-to-LDS; a run's last tile masks keys past the run's
 // end.  The compute pipeline is the one-shot kernel's: S^T = K Q^T and
 // O^T += V^T P^T on v_mfma_f32_32x32x16_bf16, lazy rescale, one barrier
-// per tile.  Summary query rows of the segments run in the first
-// workgroups, one wave per (sequence, kv head, summary).
+// per tile.  Summary query rows of the segments run in a second, LDS-free
+// launch, one wave per (sequence, kv head, summary).
 #include <type_traits>
 
 #include "ksa_internal.h"
@@ -138,19 +138,21 @@ __device__ void chunk_summary_wave(const CkArgs& a, int64_t item, const ChunkPtr
 
 }  // namespace
 
+// Summary query rows of the segments: a launch of its own, with no LDS, so
+// that these short, latency-bound waves run at full occupancy.
+__global__ void __launch_bounds__(256) prefill_chunk_summary_kernel(CkArgs a, ChunkPtrs p) {
+  const int64_t item = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (item < static_cast<int64_t>(a.batch) * a.hkv * a.max_sum_seg) chunk_summary_wave(a, item, p);
+}
+
 template <int HPW>
 __global__ void __launch_bounds__(256, 2) prefill_chunk_d128_kernel(CkArgs a, ChunkPtrs p) {
   constexpr int PT = 32 * (4 / HPW);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if (static_cast<int>(blockIdx.x) < a.n_sum_blocks) {
-    const int64_t item = static_cast<int64_t>(blockIdx.x) * 4 + wave;
-    if (item < static_cast<int64_t>(a.batch) * a.hkv * a.max_sum_seg) chunk_summary_wave(a, item, p);
-    return;
-  }
   const int n_slots = a.batch * a.hkv * a.n_hg;
-  const int bid = blockIdx.x - a.n_sum_blocks;
+  const int bid = blockIdx.x;
   const int hslot = bid % n_slots;
   const int tile = bid / n_slots;
   const int hg = hslot % a.n_hg;
@@ -459,8 +461,11 @@ static hipError_t launch_hpw(const ChunkArgs& c, const ChunkPtrs& p, hipStream_t
   a.total_rows = c.total_rows;
   const int64_t sum_items = static_cast<int64_t>(a.batch) * a.hkv * a.max_sum_seg;
   a.n_sum_blocks = static_cast<int32_t>((sum_items + 3) / 4);
-  const int64_t blocks = static_cast<int64_t>(a.batch) * a.hkv * a.n_hg * a.n_tiles + a.n_sum_blocks;
+  const int64_t blocks = static_cast<int64_t>(a.batch) * a.hkv * a.n_hg * a.n_tiles;
   hipLaunchKernelGGL(prefill_chunk_d128_kernel<HPW>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, s, a, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.n_sum_blocks == 0) return e;
+  hipLaunchKernelGGL(prefill_chunk_summary_kernel, dim3(static_cast<uint32_t>(a.n_sum_blocks)), dim3(256), 0, s, a, p);
   return hipGetLastError();
 }
 
