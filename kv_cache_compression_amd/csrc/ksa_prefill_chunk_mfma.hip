@@ -154,7 +154,7 @@ __global__ void __launch_bounds__(256, 2) prefill_chunk_d128_kernel(CkArgs a, Ch
   const int n_slots = a.batch * a.hkv * a.n_hg;
   const int bid = blockIdx.x;
   const int hslot = bid % n_slots;
-  const int tile = bid / n_slots;
+  const int tile = a.n_tiles - 1 - bid / n_slots;  // later positions (more keys) first
   const int hg = hslot % a.n_hg;
   const int kvh = (hslot / a.n_hg) % a.hkv;
   const int b = hslot / (a.n_hg * a.hkv);
