@@ -275,6 +275,8 @@ def main() -> int:
         res["roofline"]["traffic_detail"] = traffic
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
+        if not args.no_extra:
+            extra_oracle_rates(res, w)
     print(json.dumps(res), flush=True)
     return 0
 
@@ -467,6 +469,9 @@ def prefill_mla(ksa, ksa_synth, torch, dev, stream, reps: int = 5) -> dict:
             "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4), "flops": fl}
 
 
+_ORACLE_INPUTS: dict = {}   # the oracle's fp64 keys and values, kept for the extra lines
+
+
 def cpu_baseline(w, rows_req: int) -> dict:
     """The fp64 oracle on a bounded sample of the same prefill workload."""
     import numpy as np
@@ -485,6 +490,7 @@ def cpu_baseline(w, rows_req: int) -> dict:
     pos = O.position_ids(w.n_text, w.chunk)
     kr = O.rope_rotate(kx[0].double().numpy(), pos, w.rope_theta)
     vv = v[0].double().numpy()
+    _ORACLE_INPUTS.update(q=q[0], k=kr, v=vv, L=L)
     scale = 1.0 / math.sqrt(w.dqk)
     mask_count = lambda rows: int(O.visibility_mask_fast(w.n_text, w.chunk, w.window, rows=rows).sum())
 
@@ -499,13 +505,93 @@ def cpu_baseline(w, rows_req: int) -> dict:
 
     nrows = rows_req or 16
     rows, dt = run(nrows)
-    if not rows_req:   # scale the sample to about 15 s of oracle work
+    for _ in range(3 if not rows_req else 0):   # scale the sample to about 15 s of oracle work
+        if dt >= 10.0 or nrows >= 4096:
+            break
         nrows = int(min(4096, max(16, nrows * 15.0 / max(dt, 1e-3))))
         rows, dt = run(nrows)
     fl = 2 * (w.dqk + w.dv) * w.hq * mask_count(rows)
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"{len(rows)} evenly spaced augmented rows x {w.hq} heads of {w.name} "
                       f"(fp64, dense masked rows), {dt:.1f} s"}
+
+
+def extra_oracle_rates(res: dict, w) -> None:
+    """The fp64 oracle beside each extra line, on a few seconds of sampled
+    rows: backward terms of sampled query rows, MLA prefill rows, baseline
+    rows.  Same units as the GPU lines (FLOP over the sampled rows' pairs)."""
+    import numpy as np
+
+    import ksa_synth
+    from oracle import ksa_oracle as O
+
+    L, kn, vn = _ORACLE_INPUTS["L"], _ORACLE_INPUTS["k"], _ORACLE_INPUTS["v"]
+    scale = 1.0 / math.sqrt(w.dqk)
+    rows = np.linspace(0, L - 1, 24).astype(np.int64)
+    pairs = int(O.visibility_mask_fast(w.n_text, w.chunk, w.window, rows=rows).sum())
+    # only the sampled rows' queries and output gradients are read
+    qn = np.zeros((L, w.hq, w.dqk))
+    qn[rows] = _ORACLE_INPUTS["q"][rows].double().numpy()
+    g = np.zeros((L, w.hq, w.dv))
+    g[rows] = ksa_synth.normal((len(rows), w.hq, w.dv), w.dtype, ksa_synth.gen(w.seed + 7)).double().numpy()
+    t0 = time.perf_counter()
+    O.attention_backward_rows(qn, kn, vn, g, w.n_text, w.chunk, scale, rows, C=w.window)
+    dt = time.perf_counter() - t0
+    fl = 2 * (3 * w.dqk + 2 * w.dv) * w.hq * pairs
+    if res.get("prefill_backward"):
+        res["prefill_backward"]["cpu_oracle"] = {
+            "tflops": fl / dt / 1e12, "sample": f"backward terms of {len(rows)} rows x {w.hq} heads, {dt:.1f} s"}
+
+    for line in res.get("prefill_baselines", []):
+        mode = O.MODE_SCA if line["mode"].startswith("sliding") else O.MODE_SWA
+        W = w.window * w.chunk
+        t0 = time.perf_counter()
+        O.baseline_attention(qn, kn, vn, w.n_text, w.chunk, mode, scale, C=w.window, W=W, rows=rows)
+        dt = time.perf_counter() - t0
+        bp = int(O.baseline_mask(w.n_text, w.chunk, mode, C=w.window, W=W, rows=rows).sum())
+        line["cpu_oracle"] = {"tflops": 2 * (w.dqk + w.dv) * w.hq * bp / dt / 1e12,
+                              "sample": f"{len(rows)} rows x {w.hq} heads, {dt:.1f} s"}
+
+    mw = ksa_synth.PREFILL_MLA_8K
+    ml = O.augmented_len(mw.n_text, mw.chunk)
+    gm = ksa_synth.gen(mw.seed)
+    mrows = np.linspace(0, ml - 1, 6).astype(np.int64)
+    mq = np.zeros((ml, mw.hq, mw.dqk))
+    mq[mrows] = ksa_synth.normal((len(mrows), mw.hq, mw.dqk), mw.dtype, gm).double().numpy()
+    mk = ksa_synth.normal((ml, mw.hkv, mw.dqk), mw.dtype, gm).double().numpy()
+    t0 = time.perf_counter()
+    O.ksa_attention(mq, mk, None, mw.n_text, mw.chunk, mw.window, 1.0 / math.sqrt(mw.dqk), rows=mrows,
+                    dv=mw.dv)
+    dt = time.perf_counter() - t0
+    mp = int(O.visibility_mask_fast(mw.n_text, mw.chunk, mw.window, rows=mrows).sum())
+    if res.get("prefill_mla"):
+        res["prefill_mla"]["cpu_oracle"] = {
+            "tflops": 2 * (mw.dqk + mw.dv) * mw.hq * mp / dt / 1e12,
+            "sample": f"{len(mrows)} rows x {mw.hq} heads of {mw.name}, {dt:.1f} s"}
+
+    # one decode query per workload, against its whole logical history
+    for key, dw in (("decode", ksa_synth.DECODE_GQA), ("decode_mla", ksa_synth.DECODE_MLA)):
+        if key not in res:
+            continue
+        n = ksa_synth.decode_histories(dw)[0]
+        A = O.text_row(n - 1, dw.chunk) + 1
+        gd = ksa_synth.gen(dw.seed + 11)
+        hk = ksa_synth.normal((A, dw.hkv, dw.dqk), dw.dtype, gd).double().numpy()
+        hv = None if dw.v_is_k_prefix else ksa_synth.normal((A, dw.hkv, dw.dv), dw.dtype, gd).double().numpy()
+        # the oracle's time is linear in the query heads: time at most 16 and scale
+        nh = min(dw.hq, 16 if dw.hkv == 1 else dw.hq)
+        dq1 = ksa_synth.decode_query(dw)[0, :nh].double().numpy()
+        t0 = time.perf_counter()
+        O.decode_attention(dq1, hk, hv, n, dw.chunk, dw.window, 1.0 / math.sqrt(dw.dqk), "t", dv=dw.dv)
+        dt = (time.perf_counter() - t0) * dw.hq / nh
+        m = (n - 1) // dw.chunk
+        rows1 = n - m * dw.chunk + min(m, dw.window) * dw.chunk + max(0, m - dw.window)
+        width = dw.dqk if dw.v_is_k_prefix else dw.dqk + dw.dv
+        nbytes = rows1 * dw.hkv * width * 2 + dw.hq * (dw.dqk + dw.dv) * 2
+        res[key]["cpu_oracle"] = {"gbps": nbytes / dt / 1e9,
+                                  "sample": f"one {n}-token sequence of {dw.name}, {nh} of {dw.hq} "
+                                            f"query heads timed, {dt:.2f} s scaled"}
+        del hk, hv
 
 
 if __name__ == "__main__":
