@@ -212,7 +212,8 @@ def main() -> int:
         step(e)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    seg_ms = {s: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps for i, s in enumerate(segs)}
+    seg_all = {s: sorted(e[i].elapsed_time(e[i + 1]) for e in evs) for i, s in enumerate(segs)}
+    seg_ms = {s: sum(v) / args.steps for s, v in seg_all.items()}
     for c in [dcache] + mcaches:
         errs = ksa.ksa_cache_read_errors(c)
         if any(errs):
@@ -265,10 +266,17 @@ def main() -> int:
         "prefill_mla": mla_pre,
         "rope": {"value": round(rope_gbps, 1), "unit": "GB/s", "ms": round(seg_ms["rope"], 4)},
         "breakdown_ms": {s: round(v, 4) for s, v in seg_ms.items()},
+        "breakdown_ms_min": {s: round(v[0], 4) for s, v in seg_all.items()},
+        "breakdown_ms_median": {s: round(v[len(v) // 2], 4) for s, v in seg_all.items()},
         "roofline": {"kernel": "prefill_mfma_d128_kernel", "bound": "mfma", "achieved": round(pre_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": None},
     }
+    peaks = machine_peaks(torch, dev, stream)
+    if peaks:
+        res["machine_peaks"] = peaks
+        res["roofline"]["frac_of_measured_peak"] = round(pre_tflops / peaks["mfma_bf16_tflops"], 4)
+        res["decode"]["frac_of_measured_read"] = round(dec_gbps / peaks["hbm_read_gbps"], 4)
     traffic = prefill_traffic()
     if traffic is not None:
         res["roofline"]["traffic"] = traffic["total_bytes"]
@@ -284,6 +292,51 @@ def main() -> int:
 COPY_PROBE_BYTES = 256 << 20
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "prefill_mfma_d128_32k_pmc.txt")
 PREFILL_SOURCE = os.path.join(ROOT, "kv_cache_compression_amd", "csrc", "ksa_prefill_mfma.hip")
+
+
+def machine_peaks(torch, dev, stream) -> dict:
+    """Measured ceilings of this GPU: the bf16 MFMA issue loop and the
+    streaming HBM read and copy of libksa_probe.so, best of three launches
+    each, timed with HIP events on the benchmark stream."""
+    try:
+        from kv_cache_compression_amd import probe
+        probe.lib()
+    except Exception as e:  # the attention numbers stand without it
+        print(f"machine-peak probes unavailable: {e}", file=sys.stderr)
+        return {}
+
+    def best_ms(fn, reps=3):
+        fn()
+        out = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1))
+        return min(out)
+
+    blocks, iters = 2048, 512
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    flops = probe.lib().ksa_probe_mfma_bf16_flops(blocks, iters)
+    ms = best_ms(lambda: probe.ksa_probe_mfma_bf16(blocks, iters, sink, stream))
+    mfma = flops / (ms * 1e-3) / 1e12
+    nbytes = 4 << 30        # 16 x the 256 MB last-level cache
+    src = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+    rd = {}
+    for nb in (1024, 2048, 4096):
+        isink = torch.empty(nb * 256, dtype=torch.int32, device=dev)
+        rd[nb] = nbytes / (best_ms(lambda: probe.ksa_probe_hbm_read(src, nb, isink, stream)) * 1e-3) / 1e9
+    half = src[: nbytes // 2]
+    dst = torch.empty(nbytes // 2, dtype=torch.uint8, device=dev)
+    cp = nbytes / (best_ms(lambda: probe.ksa_probe_hbm_copy(half, dst, 2048, stream)) * 1e-3) / 1e9
+    del src, dst, half
+    torch.cuda.empty_cache()
+    return {"mfma_bf16_tflops": round(mfma, 1), "hbm_read_gbps": round(max(rd.values()), 1),
+            "hbm_copy_gbps": round(cp, 1),
+            "source": "libksa_probe.so: 32x32x16 bf16 MFMA loop (2048 x 256 threads), 4 GiB non-temporal "
+                      "read, 2 GiB copy (read + write counted); best of 3"}
 
 
 def copy_probe() -> int:

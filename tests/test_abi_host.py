@@ -36,6 +36,28 @@ def test_exports_every_declared_symbol(L):
         assert hasattr(L, name), name
 
 
+def test_probe_library_exports_every_declared_symbol():
+    """The machine-peak probes (include/ksa_probe.h) live in their own library."""
+    from kv_cache_compression_amd import probe
+    if not os.path.exists(probe.PROBE_LIB_PATH):
+        from kv_cache_compression_amd import _build
+        _build.build()
+    txt = open(os.path.join(ROOT, "include", "ksa_probe.h")).read()
+    decl = sorted(set(re.findall(r"^\w[\w ]*?\b(ksa_probe_\w+)\s*\(", txt, re.M)))
+    assert decl == sorted(probe.EXPORTS)
+    PL = probe.lib()
+    for name in decl:
+        assert hasattr(PL, name), name
+    # host-side argument checks: nothing is launched
+    assert PL.ksa_probe_mfma_bf16(0, 1, None, None) == -1
+    assert PL.ksa_probe_hbm_read(None, 16, 1, None, None) == -1
+    assert PL.ksa_probe_hbm_copy(None, None, 16, 1, None) == -1
+    assert PL.ksa_probe_mfma_bf16_flops(2, 3) == 2 * 4 * 3 * 4 * 2 * 32 * 32 * 16
+    # the attention library holds none of them
+    K_syms = open(K.LIB_PATH, "rb").read()
+    assert b"ksa_probe_mfma_bf16" not in K_syms
+
+
 def _params(**kw):
     d = dict(chunk_size=8, window_chunks=4, num_q_heads=4, num_kv_heads=2, head_dim_qk=64,
              head_dim_v=64, v_is_k_prefix=0, softmax_scale=0.125, dtype=K.KSA_DTYPE_FP32)
