@@ -317,7 +317,7 @@ def machine_peaks(torch, dev, stream) -> dict:
             out.append(e0.elapsed_time(e1))
         return min(out)
 
-    blocks, iters = 2048, 512
+    blocks, iters = 2048, 2048
     sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
     flops = probe.lib().ksa_probe_mfma_bf16_flops(blocks, iters)
     ms = best_ms(lambda: probe.ksa_probe_mfma_bf16(blocks, iters, sink, stream))
@@ -325,18 +325,20 @@ def machine_peaks(torch, dev, stream) -> dict:
     nbytes = 4 << 30        # 16 x the 256 MB last-level cache
     src = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
     rd = {}
-    for nb in (1024, 2048, 4096):
+    for nb in (512, 2048, 8192):
         isink = torch.empty(nb * 256, dtype=torch.int32, device=dev)
         rd[nb] = nbytes / (best_ms(lambda: probe.ksa_probe_hbm_read(src, nb, isink, stream)) * 1e-3) / 1e9
     half = src[: nbytes // 2]
     dst = torch.empty(nbytes // 2, dtype=torch.uint8, device=dev)
-    cp = nbytes / (best_ms(lambda: probe.ksa_probe_hbm_copy(half, dst, 2048, stream)) * 1e-3) / 1e9
+    cp = max(nbytes / (best_ms(lambda: probe.ksa_probe_hbm_copy(half, dst, nb, stream)) * 1e-3) / 1e9
+             for nb in (512, 2048, 8192))
     del src, dst, half
     torch.cuda.empty_cache()
     return {"mfma_bf16_tflops": round(mfma, 1), "hbm_read_gbps": round(max(rd.values()), 1),
             "hbm_copy_gbps": round(cp, 1),
-            "source": "libksa_probe.so: 32x32x16 bf16 MFMA loop (2048 x 256 threads), 4 GiB non-temporal "
-                      "read, 2 GiB copy (read + write counted); best of 3"}
+            "source": "libksa_probe.so: 32x32x16 bf16 MFMA loop (2048 x 256 threads, 2048 iterations), "
+                      "4 GiB non-temporal read and 2 GiB copy (read + write counted) at 512/2048/8192 "
+                      "workgroups; best of 3 launches each"}
 
 
 def copy_probe() -> int:
