@@ -320,8 +320,16 @@ def machine_peaks(torch, dev, stream) -> dict:
     blocks, iters = 2048, 2048
     sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
     flops = probe.lib().ksa_probe_mfma_bf16_flops(blocks, iters)
-    ms = best_ms(lambda: probe.ksa_probe_mfma_bf16(blocks, iters, sink, stream))
+    ms = best_ms(lambda: probe.ksa_probe_mfma_bf16(blocks, iters, sink, None, stream))
     mfma = flops / (ms * 1e-3) / 1e12
+    # the same loop on N(0,1) bf16 operands, as the attention kernels see them
+    nel = probe.lib().ksa_probe_mfma_bf16_operand_bytes(blocks) // 2
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    opnd = torch.randn(nel, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    ms = best_ms(lambda: probe.ksa_probe_mfma_bf16(blocks, iters, sink, opnd, stream))
+    mfma_data = flops / (ms * 1e-3) / 1e12
+    del opnd
     nbytes = 4 << 30        # 16 x the 256 MB last-level cache
     src = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
     rd = {}
@@ -334,9 +342,11 @@ def machine_peaks(torch, dev, stream) -> dict:
              for nb in (512, 2048, 8192))
     del src, dst, half
     torch.cuda.empty_cache()
-    return {"mfma_bf16_tflops": round(mfma, 1), "hbm_read_gbps": round(max(rd.values()), 1),
+    return {"mfma_bf16_tflops": round(mfma_data, 1), "mfma_bf16_tflops_constant_operands": round(mfma, 1),
+            "hbm_read_gbps": round(max(rd.values()), 1),
             "hbm_copy_gbps": round(cp, 1),
-            "source": "libksa_probe.so: 32x32x16 bf16 MFMA loop (2048 x 256 threads, 2048 iterations), "
+            "source": "libksa_probe.so: 32x32x16 bf16 MFMA loop (2048 x 256 threads, 2048 iterations) on "
+                      "N(0,1) operands (and on lane-index constants), "
                       "4 GiB non-temporal read and 2 GiB copy (read + write counted) at 512/2048/8192 "
                       "workgroups; best of 3 launches each"}
 

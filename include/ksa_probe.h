@@ -19,12 +19,18 @@ extern "C" {
 #endif
 
 /* bf16 matrix-core issue loop: `blocks` workgroups of 256 threads (two per
- * SIMD at most), each wave issuing `iters` x 4 independent
- * v_mfma_f32_32x32x16_bf16 on register operands.  sink: [blocks * 256] fp32,
- * written once per thread (keeps the loop live).  The FLOP count of one
- * launch is ksa_probe_mfma_bf16_flops(blocks, iters). */
-int32_t ksa_probe_mfma_bf16(int32_t blocks, int32_t iters, float* sink, hipStream_t stream);
+ * SIMD at most), each wave issuing `iters` (even) x 4 independent
+ * v_mfma_f32_32x32x16_bf16 on register operands.  operands: NULL (values
+ * derived from the lane index, identical every iteration) or a 16-byte
+ * aligned device buffer of ksa_probe_mfma_bf16_operand_bytes(blocks) bytes
+ * of bf16 data, from which every lane takes 8 operand pairs and cycles
+ * through them.  sink: [blocks * 256] fp32, written once per thread (keeps
+ * the loop live).  The FLOP count of one launch is
+ * ksa_probe_mfma_bf16_flops(blocks, iters). */
+int32_t ksa_probe_mfma_bf16(int32_t blocks, int32_t iters, const void* operands, float* sink,
+                            hipStream_t stream);
 double ksa_probe_mfma_bf16_flops(int32_t blocks, int32_t iters);
+size_t ksa_probe_mfma_bf16_operand_bytes(int32_t blocks);
 
 /* Streaming read of `bytes` (a multiple of 16, 16-byte aligned) from src
  * with 16-byte non-temporal loads, grid-stride over `blocks` workgroups of

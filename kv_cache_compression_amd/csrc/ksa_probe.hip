@@ -2,7 +2,11 @@
 //   - a bf16 MFMA issue loop (v_mfma_f32_32x32x16_bf16, register operands,
 //     four independent accumulation chains per wave, two waves per SIMD), the
 //     sustained matrix rate of the chip under the same launch shape as the
-//     prefill kernels;
+//     prefill kernels.  The operands either derive from the lane index (the
+//     same values every iteration) or cycle through eight operand pairs
+//     loaded from a buffer of the caller's data: the matrix cores draw more
+//     power, and the clock drops, when the operand bits toggle as they do on
+//     real tensors;
 //   - a streaming HBM read (16-byte non-temporal loads, eight in flight per
 //     thread), the access pattern of the split-K decode;
 //   - a streaming HBM copy (16-byte loads and stores).
@@ -23,22 +27,41 @@ constexpr int kThreads = 256;
 constexpr int kChains = 4;
 constexpr int kUnroll = 8;
 
-__global__ void __launch_bounds__(kThreads, 2) probe_mfma_kernel(int32_t iters, float* __restrict__ sink) {
+constexpr int kPairs = 8;  // operand pairs cycled through when loaded from data
+
+__global__ void __launch_bounds__(kThreads, 2) probe_mfma_kernel(int32_t iters, const bf16x8_t* __restrict__ opnd,
+                                                                float* __restrict__ sink) {
   const int lane = threadIdx.x & 63;
-  bf16x8_t a, b;
+  bf16x8_t a[kPairs], b[kPairs];
+  if (opnd != nullptr) {
+    // 2 kPairs operands of 16 bytes per lane, distinct per wave
+    const bf16x8_t* p = opnd + (static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x) * (2 * kPairs);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    a[i] = static_cast<__bf16>(0.001f * static_cast<float>(lane + i));
-    b[i] = static_cast<__bf16>(0.001f * static_cast<float>(i - lane));
+    for (int i = 0; i < kPairs; ++i) {
+      a[i] = p[2 * i];
+      b[i] = p[2 * i + 1];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kPairs; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        a[i][j] = static_cast<__bf16>(0.001f * static_cast<float>(lane + j));
+        b[i][j] = static_cast<__bf16>(0.001f * static_cast<float>(j - lane));
+      }
   }
   f32x16_t acc[kChains];
 #pragma unroll
   for (int c = 0; c < kChains; ++c)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[c][r] = 0.f;
-  for (int it = 0; it < iters; ++it) {
+  for (int it = 0; it < iters; it += 2) {
 #pragma unroll
-    for (int c = 0; c < kChains; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+    for (int u = 0; u < 2 * kChains; ++u) {
+      const int c = u % kChains;
+      const int pr = u % kPairs;
+      acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[pr], b[pr], acc[c], 0, 0, 0);
+    }
   }
   float s = 0.f;
 #pragma unroll
@@ -92,11 +115,18 @@ __attribute__((visibility("default"))) double ksa_probe_mfma_bf16_flops(int32_t 
   return static_cast<double>(blocks) * (kThreads / 64) * iters * kChains * 2.0 * 32 * 32 * 16;
 }
 
-__attribute__((visibility("default"))) int32_t ksa_probe_mfma_bf16(int32_t blocks, int32_t iters, float* sink,
+__attribute__((visibility("default"))) size_t ksa_probe_mfma_bf16_operand_bytes(int32_t blocks) {
+  return blocks <= 0 ? 0 : static_cast<size_t>(blocks) * kThreads * 2 * kPairs * sizeof(bf16x8_t);
+}
+
+__attribute__((visibility("default"))) int32_t ksa_probe_mfma_bf16(int32_t blocks, int32_t iters,
+                                                                   const void* operands, float* sink,
                                                                    hipStream_t stream) {
-  if (blocks <= 0 || iters <= 0 || sink == nullptr) return -1;
+  if (blocks <= 0 || iters <= 0 || iters % 2 != 0 || sink == nullptr ||
+      reinterpret_cast<uintptr_t>(operands) % 16 != 0)
+    return -1;
   hipLaunchKernelGGL(probe_mfma_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream, iters,
-                     sink);
+                     static_cast<const bf16x8_t*>(operands), sink);
   return status_of(hipGetLastError());
 }
 

@@ -11,7 +11,8 @@ from typing import Optional
 import torch
 
 PROBE_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libksa_probe.so")
-EXPORTS = ("ksa_probe_mfma_bf16", "ksa_probe_mfma_bf16_flops", "ksa_probe_hbm_read", "ksa_probe_hbm_copy")
+EXPORTS = ("ksa_probe_mfma_bf16", "ksa_probe_mfma_bf16_flops", "ksa_probe_mfma_bf16_operand_bytes",
+           "ksa_probe_hbm_read", "ksa_probe_hbm_copy")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -23,10 +24,12 @@ def lib() -> ctypes.CDLL:
             raise RuntimeError(f"{PROBE_LIB_PATH} is not built")
         L = ctypes.CDLL(PROBE_LIB_PATH)
         vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
-        L.ksa_probe_mfma_bf16.argtypes = [i32, i32, vp, vp]
+        L.ksa_probe_mfma_bf16.argtypes = [i32, i32, vp, vp, vp]
         L.ksa_probe_mfma_bf16.restype = i32
         L.ksa_probe_mfma_bf16_flops.argtypes = [i32, i32]
         L.ksa_probe_mfma_bf16_flops.restype = ctypes.c_double
+        L.ksa_probe_mfma_bf16_operand_bytes.argtypes = [i32]
+        L.ksa_probe_mfma_bf16_operand_bytes.restype = sz
         L.ksa_probe_hbm_read.argtypes = [vp, sz, i32, vp, vp]
         L.ksa_probe_hbm_read.restype = i32
         L.ksa_probe_hbm_copy.argtypes = [vp, vp, sz, i32, vp]
@@ -44,11 +47,20 @@ def _stream(stream) -> int:
     return (stream or torch.cuda.current_stream()).cuda_stream
 
 
-def ksa_probe_mfma_bf16(blocks: int, iters: int, sink: torch.Tensor, stream=None) -> float:
-    """Launch the MFMA loop; returns the FLOP count of the launch."""
+def ksa_probe_mfma_bf16(blocks: int, iters: int, sink: torch.Tensor, operands: Optional[torch.Tensor] = None,
+                       stream=None) -> float:
+    """Launch the MFMA loop (operands from ``operands`` when given, else
+    from the lane index); returns the FLOP count of the launch."""
     if sink.dtype != torch.float32 or not sink.is_cuda or sink.numel() < blocks * 256:
         raise ValueError("sink must be a CUDA float32 tensor of blocks * 256 elements")
-    _check(lib().ksa_probe_mfma_bf16(blocks, iters, sink.data_ptr(), _stream(stream)), "ksa_probe_mfma_bf16")
+    optr = None
+    if operands is not None:
+        need = lib().ksa_probe_mfma_bf16_operand_bytes(blocks)
+        if (not operands.is_cuda or not operands.is_contiguous()
+                or operands.numel() * operands.element_size() < need):
+            raise ValueError(f"operands must be a contiguous CUDA tensor of at least {need} bytes")
+        optr = operands.data_ptr()
+    _check(lib().ksa_probe_mfma_bf16(blocks, iters, optr, sink.data_ptr(), _stream(stream)), "ksa_probe_mfma_bf16")
     return lib().ksa_probe_mfma_bf16_flops(blocks, iters)
 
 

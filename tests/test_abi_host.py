@@ -49,7 +49,9 @@ def test_probe_library_exports_every_declared_symbol():
     for name in decl:
         assert hasattr(PL, name), name
     # host-side argument checks: nothing is launched
-    assert PL.ksa_probe_mfma_bf16(0, 1, None, None) == -1
+    assert PL.ksa_probe_mfma_bf16(0, 2, None, None, None) == -1
+    assert PL.ksa_probe_mfma_bf16(1, 3, None, None, None) == -1
+    assert PL.ksa_probe_mfma_bf16_operand_bytes(2) == 2 * 256 * 16 * 16
     assert PL.ksa_probe_hbm_read(None, 16, 1, None, None) == -1
     assert PL.ksa_probe_hbm_copy(None, None, 16, 1, None) == -1
     assert PL.ksa_probe_mfma_bf16_flops(2, 3) == 2 * 4 * 3 * 4 * 2 * 32 * 32 * 16
