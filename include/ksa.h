@@ -111,13 +111,15 @@ KSA_API int64_t ksa_augmented_len(int64_t n_text, int32_t chunk_size);
 /* Half-split RoPE in place over the augmented sequence, positions by the
  * KSA rule: text t_i -> i, summary s_j -> j*k + k - 1 (Sec. 2.2.1).
  * x: [batch, L, num_heads, head_dim] in p->dtype.  Dims [rot_off,
- * rot_off+rot_dim) are rotated, rot_dim even.  Angles are formed in fp64. */
+ * rot_off+rot_dim) are rotated, rot_dim even.  Angles are formed in fp64.
+ * batch == 0 or n_text == 0 is a no-op (x may then be NULL). */
 KSA_API int32_t ksa_rope_augmented(const ksa_params* p, int32_t batch, int64_t n_text, void* x,
                            int32_t num_heads, int32_t head_dim, int32_t rot_off, int32_t rot_dim,
                            double theta, void* stream);
 
 /* Same rotation with explicit positions: x [rows, num_heads, head_dim],
- * positions [rows] int64 (device).  Used for decode tokens. */
+ * positions [rows] int64 (device).  Used for decode tokens.  rows == 0 is a
+ * no-op (x and positions may then be NULL). */
 KSA_API int32_t ksa_rope_positions(const ksa_params* p, int64_t rows, const int64_t* positions, void* x,
                            int32_t num_heads, int32_t head_dim, int32_t rot_off, int32_t rot_dim,
                            double theta, void* stream);

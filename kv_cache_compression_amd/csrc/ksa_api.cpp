@@ -113,13 +113,14 @@ int64_t ksa_augmented_len(int64_t n_text, int32_t k) {
 
 static int32_t rope_common(const ksa_params* p, ksa::RopeArgs& ra, void* x, void* stream) {
   if (int32_t st = check_params(p)) return st;
-  if (!x) return fail(KSA_STATUS_INVALID_ARGUMENT, "x is NULL");
   if (ra.heads < 1 || ra.head_dim < 1) return fail(KSA_STATUS_INVALID_ARGUMENT, "bad heads/head_dim");
   if (ra.rot_dim < 2 || (ra.rot_dim & 1) || ra.rot_off < 0 || ra.rot_off + ra.rot_dim > ra.head_dim)
     return fail(KSA_STATUS_INVALID_ARGUMENT, "rotary block [%d, %d) does not fit head_dim %d (even width)",
                 ra.rot_off, ra.rot_off + ra.rot_dim, ra.head_dim);
   if (!(ra.theta > 1.0)) return fail(KSA_STATUS_INVALID_ARGUMENT, "theta must be > 1");
   g_msg[0] = 0;
+  if (ra.batch == 0 || ra.rows == 0) return KSA_STATUS_OK;  // empty input: nothing to rotate
+  if (!x) return fail(KSA_STATUS_INVALID_ARGUMENT, "x is NULL");
   return hip_status(ksa::launch_rope(ra, x, p->dtype, static_cast<hipStream_t>(stream)), "rope");
 }
 
@@ -146,7 +147,7 @@ int32_t ksa_rope_positions(const ksa_params* p, int64_t rows, const int64_t* pos
                            int32_t num_heads, int32_t head_dim, int32_t rot_off, int32_t rot_dim,
                            double theta, void* stream) {
   if (rows < 0) return fail(KSA_STATUS_INVALID_ARGUMENT, "negative rows");
-  if (!positions) return fail(KSA_STATUS_INVALID_ARGUMENT, "positions is NULL");
+  if (rows > 0 && !positions) return fail(KSA_STATUS_INVALID_ARGUMENT, "positions is NULL");
   if (int32_t st = check_params(p)) return st;
   ksa::RopeArgs ra;
   ra.batch = 1;

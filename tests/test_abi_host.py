@@ -165,6 +165,23 @@ def test_chunk_and_append_rows_arguments(L):
     assert L.ksa_cache_append_rows(ctypes.byref(p), ctypes.byref(c), 0, None, 10, None, None, None) == 0
 
 
+def test_rope_empty_inputs_are_no_ops(L):
+    p = _params()
+    fake = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    assert L.ksa_rope_augmented(ctypes.byref(p), 1, 0, None, 4, 64, 0, 64, ctypes.c_double(1e6), None) == 0
+    assert L.ksa_rope_augmented(ctypes.byref(p), 0, 100, None, 4, 64, 0, 64, ctypes.c_double(1e6), None) == 0
+    rc, msg = _status(L, L.ksa_rope_augmented(ctypes.byref(p), 1, 10, None, 4, 64, 0, 64, ctypes.c_double(1e6),
+                                              None))
+    assert rc == 1 and "NULL" in msg
+    # argument errors are still reported for an empty input
+    rc, _ = _status(L, L.ksa_rope_augmented(ctypes.byref(p), 1, 0, None, 4, 64, 0, 63, ctypes.c_double(1e6), None))
+    assert rc == 1
+    assert L.ksa_rope_positions(ctypes.byref(p), 0, None, None, 4, 64, 0, 64, ctypes.c_double(1e6), None) == 0
+    rc, msg = _status(L, L.ksa_rope_positions(ctypes.byref(p), 3, None, fake, 4, 64, 0, 64, ctypes.c_double(1e6),
+                                              None))
+    assert rc == 1 and "positions" in msg
+
+
 def test_cache_argument_checks(L):
     p = _params()
     fake = ctypes.c_void_p(16)

@@ -1,0 +1,100 @@
+"""Degenerate inputs through the C ABI on the GPU: empty sequences and
+batches, a single token, exactly one chunk, a window wider than the
+sequence, and empty cache segments.  Values are checked against the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_compression_amd as ksa
+import ksa_synth
+from oracle import ksa_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    return torch.device("cuda:0")
+
+
+SHAPES = [(torch.bfloat16, 128, 8, 2), (torch.float32, 64, 4, 2)]
+
+
+@pytest.mark.parametrize("dtype,D,hq,hkv", SHAPES)
+def test_empty_sequence_and_batch(dtype, D, hq, hkv):
+    dev = _dev()
+    p = ksa.Params(8, 4, hq, hkv, D, D, dtype)
+    for B, n in ((1, 0), (0, 0), (0, 40)):
+        L = O.augmented_len(n, 8)
+        q = torch.zeros((B, L, hq, D), dtype=dtype, device=dev)
+        k = torch.zeros((B, L, hkv, D), dtype=dtype, device=dev)
+        v = torch.zeros((B, L, hkv, D), dtype=dtype, device=dev)
+        lse = torch.zeros((B, hq, L), dtype=torch.float32, device=dev)
+        for mode, W in ((ksa.MODE_KSA, 0), (ksa.MODE_SCA, 0), (ksa.MODE_SWA, 5)):
+            out = ksa.ksa_prefill_attn_mode(p, mode, W, q, k, v, n, lse=lse)
+            assert out.shape == (B, L, hq, D)
+            dq, dk, dv = ksa.ksa_prefill_attn_bwd(p, mode, W, q, k, v, out, out, lse, n)
+            assert dq.shape == q.shape and dk.shape == k.shape and dv.shape == v.shape
+        ksa.ksa_rope_augmented(p, q, n, 1e6)
+    torch.cuda.synchronize()
+
+
+def _oracle_case(dtype, D, hq, hkv, n, k, C, seed):
+    w = ksa_synth.PrefillWorkload("edge", 1, n, k, C, hq, hkv, D, D, dtype, 1e6, seed)
+    L = O.augmented_len(n, k)
+    q, kx, v = ksa_synth.prefill_qkv(w, L)
+    p = ksa.Params(k, C, hq, hkv, D, D, dtype)
+    dev = _dev()
+    lse = torch.empty((1, hq, L), dtype=torch.float32, device=dev)
+    out = ksa.ksa_prefill_attn(p, q.to(dev), kx.to(dev), v.to(dev), n, lse=lse)
+    torch.cuda.synchronize()
+    ref, ref_lse = O.ksa_attention(q[0].double().numpy(), kx[0].double().numpy(), v[0].double().numpy(),
+                                   n, k, C, p.scale)
+    got = out[0].float().cpu().numpy()
+    err = np.abs(got - ref)
+    lerr = np.abs(lse[0].cpu().numpy() - ref_lse)   # both [Hq, L]
+    if dtype == torch.float32:
+        assert err.max() <= 1e-4 and lerr.max() <= 1e-4, (err.max(), lerr.max())
+    else:
+        assert err.max() <= 2e-2 and err.mean() <= 2e-3, (err.max(), err.mean())
+        assert lerr.max() <= 2e-2, lerr.max()
+
+
+@pytest.mark.parametrize("dtype,D,hq,hkv", SHAPES)
+@pytest.mark.parametrize("n,k,C", [
+    (1, 8, 4),      # one text token, no complete chunk
+    (1, 1, 0),      # one token that completes a chunk: text row + its summary
+    (8, 8, 0),      # exactly one chunk, no window
+    (8, 8, 4),      # exactly one chunk
+    (100, 4, 1000), # window wider than the sequence: causal text + own-chunk summaries
+    (65, 64, 1),    # chunk wider than a key tile, ragged tail of one token
+])
+def test_degenerate_prefills_match_oracle(dtype, D, hq, hkv, n, k, C):
+    _oracle_case(dtype, D, hq, hkv, n, k, C, seed=n * 31 + k)
+
+
+def test_empty_cache_segments_are_no_ops():
+    dev = _dev()
+    k, C, hq, hkv, D = 4, 2, 4, 2, 32
+    p = ksa.Params(k, C, hq, hkv, D, D, torch.float32)
+    c = ksa.Cache(p, 2, 8, device=dev)
+    ksa.ksa_cache_reset(c)
+    g = torch.Generator(device=dev)
+    g.manual_seed(3)
+    c.k.normal_(generator=g)
+    c.v.normal_(generator=g)
+    st = torch.tensor([[3, 2, 0, 0], [0, 0, 0, 0]], dtype=torch.int32, device=dev)
+    c.state.copy_(st)
+    k0, v0 = c.k.clone(), c.v.clone()
+    seg = torch.zeros(3, dtype=torch.int64, device=dev)
+    rows = torch.zeros((0, hkv, D), dtype=torch.float32, device=dev)
+    ksa.ksa_cache_append_rows(c, seg, 0, rows, rows)
+    qr = torch.zeros((0, hq, D), dtype=torch.float32, device=dev)
+    out = ksa.ksa_prefill_chunk(c, seg, 0, qr, rows, rows)
+    torch.cuda.synchronize()
+    assert out.shape == (0, hq, D)
+    assert torch.equal(c.state, st)
+    assert torch.equal(c.k, k0) and torch.equal(c.v, v0)
+    assert ksa.ksa_cache_read_errors(c) == [0, 0]
