@@ -45,7 +45,9 @@ def _compare(name, got, ref, bf16):
     rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
     print(f"  {name}: max {e.max():.3e} rel-l2 {rel:.3e} |ref|max {np.abs(ref).max():.2f}", flush=True)
     assert np.all(e <= tol * (1 + np.abs(ref))), name
-    if bf16:
+    # a relative error needs a reference away from zero: rows that see a
+    # single key have dS = P (dP - Delta) = 0 exactly, so dq and dk vanish
+    if bf16 and np.linalg.norm(ref) > 1e-3:
         assert rel <= 1.5e-2, name
 
 
@@ -92,6 +94,10 @@ def test_bwd_bf16_generic_d64():
     (1000, 8, 4, 8, 2, O.MODE_SWA, 129, 1),
     (2100, 8, 16, 16, 4, O.MODE_KSA, 0, 1),
     (5000, 8, 4, 8, 2, O.MODE_KSA, 0, 1),
+    (1, 8, 4, 4, 1, O.MODE_KSA, 0, 1),      # one text token
+    (1, 1, 0, 4, 1, O.MODE_KSA, 0, 1),      # one token completing a chunk (text row + summary)
+    (8, 8, 0, 4, 2, O.MODE_KSA, 0, 1),      # exactly one chunk
+    (65, 64, 1, 4, 2, O.MODE_KSA, 0, 1),    # chunk wider than a key tile
 ])
 def test_bwd_bf16_mfma(n, k, C, hq, hkv, mode, W, batch):
     _case(torch.bfloat16, 128, n, k, C, hq, hkv, mode, W, batch, 1000 + n + mode)
