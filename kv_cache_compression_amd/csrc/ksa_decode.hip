@@ -321,6 +321,7 @@ __global__ void __launch_bounds__(256) decode_gqa_d128_split_kernel(
 // Merge the split partials of one (sequence, query head) per workgroup.
 template <typename T>
 __global__ void __launch_bounds__(128) decode_merge_kernel(DecodeArgs a, int nsplit,
+                                                           int32_t* __restrict__ state,
                                                            const int32_t* __restrict__ kind,
                                                            const float* __restrict__ ws,
                                                            T* __restrict__ out,
@@ -328,6 +329,10 @@ __global__ void __launch_bounds__(128) decode_merge_kernel(DecodeArgs a, int nsp
   const int hq = blockIdx.x;
   const int b = blockIdx.y;
   if (kind[b] < 0) return;
+  // error flag for a summary read that finds no freshly committed chunk (the
+  // split kernel has read the state by now)
+  if (hq == 0 && threadIdx.x == 0 && !decode_slice(state + 4 * b, kind[b], a.k, a.C, a.max_summaries).ok)
+    state[4 * b + 3] |= KSA_CACHE_ERR_BAD_SUMMARY_READ;
   const int D = a.dv;
   const float* rec = ws + (static_cast<int64_t>(b) * a.hq + hq) * nsplit * (D + 2);
   float mx = kNegInf;
@@ -343,15 +348,6 @@ __global__ void __launch_bounds__(128) decode_merge_kernel(DecodeArgs a, int nsp
   }
   if (lse && threadIdx.x == 0)
     lse[static_cast<int64_t>(b) * a.hq + hq] = l > 0.f ? (mx + log2f(l)) * kLn2 : kNegInf;
-}
-
-// Error flag for summary reads that find no freshly committed chunk.
-__global__ void decode_check_kernel(int32_t batch, int32_t k, int32_t C, int32_t max_summaries,
-                                    int32_t* state, const int32_t* kind) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= batch || kind[b] < 0) return;
-  const Slice sl = decode_slice(state + 4 * b, kind[b], k, C, max_summaries);
-  if (!sl.ok) state[4 * b + 3] |= KSA_CACHE_ERR_BAD_SUMMARY_READ;
 }
 
 static bool gqa_fast_ok(const DecodeArgs& a, int32_t dtype) {
@@ -397,10 +393,7 @@ hipError_t launch_decode(const DecodeArgs& a, int32_t dtype, const void* ck, con
       return launch_decode_generic<float>(a, ck, cv, st, q, kind, out, lse, s);
     return launch_decode_generic<bf16_t>(a, ck, cv, st, q, kind, out, lse, s);
   }
-  hipLaunchKernelGGL(decode_check_kernel, dim3((a.batch + 255) / 256), dim3(256), 0, s, a.batch,
-                     a.k, a.C, a.max_summaries, st, kind);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
   const int ns = choose_splits(a);
   float* w = static_cast<float*>(ws);
   switch (a.hq / a.hkv) {
@@ -411,7 +404,7 @@ hipError_t launch_decode(const DecodeArgs& a, int32_t dtype, const void* ck, con
     default: e = launch_gqa<16>(a, ns, ck, cv, state, q, kind, w, s); break;
   }
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_merge_kernel<bf16_t>, dim3(a.hq, a.batch), dim3(128), 0, s, a, ns, kind,
+  hipLaunchKernelGGL(decode_merge_kernel<bf16_t>, dim3(a.hq, a.batch), dim3(128), 0, s, a, ns, st, kind,
                      w, static_cast<bf16_t*>(out), lse);
   return hipGetLastError();
 }

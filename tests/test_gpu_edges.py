@@ -98,3 +98,27 @@ def test_empty_cache_segments_are_no_ops():
     assert torch.equal(c.state, st)
     assert torch.equal(c.k, k0) and torch.equal(c.v, v0)
     assert ksa.ksa_cache_read_errors(c) == [0, 0]
+
+
+@pytest.mark.parametrize("hq,hkv,dqk,dv,mla", [(8, 2, 128, 128, False), (128, 1, 576, 512, True)])
+def test_split_k_paths_flag_a_bad_summary_read(hq, hkv, dqk, dv, mla):
+    """The split-K decode paths (GQA d = 128 and absorbed MLA) flag a summary
+    query that finds no freshly committed chunk and leave the others alone."""
+    dev = _dev()
+    k, C = 8, 4
+    p = ksa.Params(k, C, hq, hkv, dqk, dv, torch.bfloat16, v_is_k_prefix=mla)
+    c = ksa.Cache(p, 3, 16, device=dev)
+    ksa.ksa_cache_reset(c)
+    c.k.zero_()
+    if c.v is not None:
+        c.v.zero_()
+    # seq 0: empty cache, summary query (bad); seq 1: 3 chunks committed and 2
+    # tokens in the current chunk, text query (fine); seq 2: skipped
+    c.state.copy_(torch.tensor([[0, 0, 0, 0], [3, 2, 0, 0], [0, 0, 0, 0]], dtype=torch.int32, device=dev))
+    q = torch.zeros((3, hq, dqk), dtype=torch.bfloat16, device=dev)
+    out = ksa.ksa_decode_attn(c, q, torch.tensor([1, 0, -1], dtype=torch.int32, device=dev))
+    torch.cuda.synchronize()
+    err = ksa.ksa_cache_read_errors(c)
+    assert err[0] & ksa.KSA_CACHE_ERR_BAD_SUMMARY_READ
+    assert err[1] == 0 and err[2] == 0
+    assert torch.isfinite(out[1].float()).all()
