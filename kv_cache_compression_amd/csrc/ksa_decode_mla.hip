@@ -168,11 +168,35 @@ __device__ MlaItem mla_item(const MlaArgs& a, const int32_t* state, const int32_
   return it;
 }
 
+// The cut per sequence for the merge: {first range, number of ranges},
+// written by one wave of the first workgroup of the split launch.
+__device__ void mla_write_cut(const MlaArgs& a, const int32_t* state, const int32_t* kind, int2* hdr) {
+  const int lane = threadIdx.x & 63;
+  const int per = mla_per(a, state, kind);
+  int first = 0;
+  for (int b0 = 0; b0 < a.batch; b0 += 64) {
+    const int b = b0 + lane;
+    const int nsp = (seq_len(a, state, kind, b) + per - 1) / per;
+    const int incl = wave_scan(nsp);
+    if (b < a.batch) hdr[b] = make_int2(first + incl - nsp, nsp);
+    first += __shfl(incl, 63);
+  }
+}
+
 }  // namespace
+
+// At most CU count + batch work items (the cut above), whatever the device.
+static constexpr int kMlaCuCap = 1024;
 
 // Record of one (work item, head): {m (log2 units), l} as two floats, then
 // 512 bf16 of the unnormalised output.
 constexpr int kMlaRec = 8 + DV * 2;
+
+// Workspace: the records of at most kMlaCuCap + batch work items, then the
+// per-sequence cut.
+__host__ __device__ inline size_t mla_cut_offset(int batch) {
+  return static_cast<size_t>(kMlaCuCap + batch) * HQ * kMlaRec;
+}
 
 __global__ void __launch_bounds__(512, 1) decode_mla_split_kernel(
     MlaArgs a, const bf16_t* __restrict__ ck, const int32_t* __restrict__ state,
@@ -184,6 +208,8 @@ __global__ void __launch_bounds__(512, 1) decode_mla_split_kernel(
   // padding per lane
   __shared__ __attribute__((aligned(16))) float xs[8][64][20];
   char* const lds[NBUF] = {lds0, lds1, lds2};
+  if (blockIdx.x == 0 && threadIdx.x < 64)
+    mla_write_cut(a, state, kind, reinterpret_cast<int2*>(ws + mla_cut_offset(a.batch)));
   const MlaItem it = mla_item(a, state, kind, blockIdx.x);
   // wave-uniform: keep them in scalar registers
   const int b = __builtin_amdgcn_readfirstlane(it.b);
@@ -371,6 +397,8 @@ __global__ void __launch_bounds__(512, 1) decode_mla_split_kernel(
 
 // One block per (head, sequence): combine the ranges of the sequence by
 // their maxima; the head-0 block also flags a slice that cannot be read.
+// Every thread owns two output columns and reads, sixteen ranges at a time,
+// each range's (maximum, sum) and its two columns in one round of loads.
 __global__ void __launch_bounds__(256) decode_mla_merge_kernel(MlaArgs a, int32_t* __restrict__ state,
                                                                const int32_t* __restrict__ kind,
                                                                const char* __restrict__ ws,
@@ -378,86 +406,50 @@ __global__ void __launch_bounds__(256) decode_mla_merge_kernel(MlaArgs a, int32_
                                                                float* __restrict__ lse) {
   const int head = blockIdx.x;
   const int b = blockIdx.y;
-  if (kind[b] < 0) return;
-  __shared__ float wgt[256];
-  __shared__ float red[2];
-  __shared__ int seq[2];  // first range of the sequence, number of ranges
-  if (threadIdx.x < 64) {
-    // the cut, as the split kernel derived it
-    const int lane = threadIdx.x;
-    const int per = mla_per(a, state, kind);
-    int first = 0, nsp_b = 0;
-    for (int b0 = 0; b0 < a.batch; b0 += 64) {
-      const int bb = b0 + lane;
-      const int nsp = (seq_len(a, state, kind, bb) + per - 1) / per;
-      const int incl = wave_scan(nsp);
-      if (b >= b0 && b < b0 + 64) {
-        const int src = b - b0;
-        first += __shfl(incl, src) - __shfl(nsp, src);
-        nsp_b = __shfl(nsp, src);
-        break;
-      }
-      first += __shfl(incl, 63);
-    }
-    if (lane == 0) {
-      seq[0] = first;
-      seq[1] = nsp_b;
-      if (head == 0 && !mla_slice(a, state + 4 * b, kind[b]).ok) state[4 * b + 3] |= KSA_CACHE_ERR_BAD_SUMMARY_READ;
-    }
-  }
-  __syncthreads();
-  const int nsp = seq[1];
-  const char* rec0 = ws + (static_cast<int64_t>(seq[0]) * HQ + head) * kMlaRec;
+  // both loads in one round trip: the cut is written for every sequence
+  const int kb = kind[b];
+  const int2 cut = reinterpret_cast<const int2*>(ws + mla_cut_offset(a.batch))[b];
+  if (kb < 0) return;
+  if (head == 0 && threadIdx.x == 0 && !mla_slice(a, state + 4 * b, kb).ok)
+    state[4 * b + 3] |= KSA_CACHE_ERR_BAD_SUMMARY_READ;
+  const int nsp = cut.y;
+  const char* rec0 = ws + (static_cast<int64_t>(cut.x) * HQ + head) * kMlaRec;
   const int64_t stride = static_cast<int64_t>(HQ) * kMlaRec;
-  // weights of every range, computed once per block into LDS
-  if (threadIdx.x < 64) {
-    float mloc = kNegInf;
-    for (int s = threadIdx.x; s < nsp; s += 64)
-      mloc = fmaxf(mloc, reinterpret_cast<const float*>(rec0 + s * stride)[0]);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o));
-    const float mu = mloc == kNegInf ? 0.f : mloc;
-    float lloc = 0.f;
-    for (int s = threadIdx.x; s < nsp; s += 64) {
-      const float* h = reinterpret_cast<const float*>(rec0 + s * stride);
-      const float w = fast_exp2(h[0] - mu);
-      if (s < 256) wgt[s] = w;
-      lloc += w * h[1];
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) lloc += __shfl_xor(lloc, o);
-    if (threadIdx.x == 0) {
-      red[0] = mloc;
-      red[1] = lloc;
-    }
-  }
-  __syncthreads();
-  const float mx = red[0], l = red[1];
-  const float mu = mx == kNegInf ? 0.f : mx;
-  const float inv = l > 0.f ? 1.f / l : 0.f;
   const int d = 2 * threadIdx.x;  // 256 threads x 2 columns = 512
-  float o0 = 0.f, o1 = 0.f;
-  // four ranges' loads in flight at a time
-  int s = 0;
-  for (; s + 4 <= nsp; s += 4) {
-    uint32_t v[4];
+  float mx = kNegInf, l = 0.f, o0 = 0.f, o1 = 0.f;
+  constexpr int G = 16;
+  for (int s0 = 0; s0 < nsp; s0 += G) {
+    float2 ml[G];
+    uint32_t v[G];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const uint32_t*>(rec0 + (s + u) * stride + 8 + 2 * d);
+    for (int u = 0; u < G; ++u) {
+      if (s0 + u < nsp) {
+        const char* r = rec0 + (s0 + u) * stride;
+        ml[u] = *reinterpret_cast<const float2*>(r);
+        v[u] = *reinterpret_cast<const uint32_t*>(r + 8 + 2 * d);
+      } else {
+        ml[u] = make_float2(kNegInf, 0.f);
+        v[u] = 0u;
+      }
+    }
+    float gm = mx;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float w = s + u < 256 ? wgt[s + u]
-                                  : fast_exp2(reinterpret_cast<const float*>(rec0 + (s + u) * stride)[0] - mu);
+    for (int u = 0; u < G; ++u) gm = fmaxf(gm, ml[u].x);
+    const float mu = gm == kNegInf ? 0.f : gm;
+    const float sc = mx == kNegInf ? 0.f : fast_exp2(mx - mu);
+    l *= sc;
+    o0 *= sc;
+    o1 *= sc;
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const float w = ml[u].x == kNegInf ? 0.f : fast_exp2(ml[u].x - mu);
+      l += w * ml[u].y;
       o0 += w * __uint_as_float(v[u] << 16);
       o1 += w * __uint_as_float(v[u] & 0xffff0000u);
     }
+    mx = gm;
   }
-  for (; s < nsp; ++s) {
-    const char* r = rec0 + s * stride;
-    const float w = s < 256 ? wgt[s] : fast_exp2(reinterpret_cast<const float*>(r)[0] - mu);
-    const uint32_t v = *reinterpret_cast<const uint32_t*>(r + 8 + 2 * d);
-    o0 += w * __uint_as_float(v << 16);
-    o1 += w * __uint_as_float(v & 0xffff0000u);
-  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
   *reinterpret_cast<uint32_t*>(out + (static_cast<int64_t>(b) * HQ + head) * DV + d) = pk_bf16(o0 * inv, o1 * inv);
   if (lse && threadIdx.x == 0)
     lse[static_cast<int64_t>(b) * HQ + head] = l > 0.f ? (mx + log2f(l)) * kLn2 : kNegInf;
@@ -468,11 +460,8 @@ bool decode_mla_supported(const DecodeArgs& a, int32_t dtype) {
          a.hkv == 1 && a.slots < (int64_t(1) << 31) / DQK;
 }
 
-// At most CU count + batch work items (the cut above), whatever the device.
-static constexpr int kMlaCuCap = 1024;
-
 size_t decode_mla_workspace_bytes(const DecodeArgs& a) {
-  return static_cast<size_t>(kMlaCuCap + a.batch) * HQ * kMlaRec;
+  return mla_cut_offset(a.batch) + static_cast<size_t>(a.batch) * sizeof(int2);
 }
 
 hipError_t launch_decode_mla(const DecodeArgs& d, const void* ck, int32_t* state, const void* q,
