@@ -13,10 +13,29 @@
 
 namespace ksa {
 
-// Copy one row of `words` 4-byte units with the whole block.
-__device__ __forceinline__ void copy_row(uint32_t* __restrict__ dst,
-                                         const uint32_t* __restrict__ src, int words) {
-  for (int w = threadIdx.x; w < words; w += blockDim.x) dst[w] = src[w];
+// Copy one K row (kw 4-byte words) and, when vd is set, one V row (vw
+// words) with the 32 lanes p = 0..31 of a group: every lane loads its words
+// of both rows (four per row per pass) before it stores any, so a copy
+// costs one memory round trip per pass.
+__device__ __forceinline__ void copy_kv_row32(uint32_t* __restrict__ kd, const uint32_t* __restrict__ ks, int kw,
+                                              uint32_t* __restrict__ vd, const uint32_t* __restrict__ vs, int vw,
+                                              int p) {
+  const int mx = kw > vw || !vd ? kw : vw;
+  for (int w0 = p; w0 < mx; w0 += 32 * 4) {
+    uint32_t a[4], c[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = w0 + 32 * u;
+      if (i < kw) a[u] = ks[i];
+      if (vd && i < vw) c[u] = vs[i];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = w0 + 32 * u;
+      if (i < kw) kd[i] = a[u];
+      if (vd && i < vw) vd[i] = c[u];
+    }
+  }
 }
 
 __global__ void cache_reset_kernel(int32_t* state, int32_t batch) {
@@ -52,7 +71,8 @@ __global__ void __launch_bounds__(256) cache_append_kernel(CacheArgs a, int kw, 
     return;
   }
   const int64_t kslot = kw, vslot = vw;  // words per slot
-  for (int h = 0; h < a.hkv; ++h) {
+  const int lane32 = threadIdx.x & 31;
+  for (int h = threadIdx.x >> 5; h < a.hkv; h += blockDim.x >> 5) {  // one 32-lane group per kv head
     const int64_t seq = static_cast<int64_t>(b) * a.hkv + h;
     uint32_t* kc = ck + seq * a.slots * kslot;
     uint32_t* vc = cv ? cv + seq * a.slots * vslot : nullptr;
@@ -60,21 +80,17 @@ __global__ void __launch_bounds__(256) cache_append_kernel(CacheArgs a, int kw, 
     const uint32_t* vn = v_new ? v_new + seq * vslot : nullptr;
     if (kd == 0) {
       const int64_t slot = a.k - r;  // current chunk fills right to left
-      copy_row(kc + slot * kslot, kn, kw);
-      if (vc) copy_row(vc + slot * vslot, vn, vw);
+      copy_kv_row32(kc + slot * kslot, kn, kw, vc ? vc + slot * vslot : nullptr, vn, vw, lane32);
     } else {
-      copy_row(kc, kn, kw);  // scratch slot 0 (Fig. 4c)
-      if (vc) copy_row(vc, vn, vw);
-      if (a.C > 0) {         // finished chunk over the oldest ring chunk (Fig. 4d)
+      copy_kv_row32(kc, kn, kw, vc, vn, vw, lane32);  // scratch slot 0 (Fig. 4c)
+      if (a.C > 0) {  // finished chunk over the oldest ring chunk (Fig. 4d)
         const int64_t dst = 1 + a.k + static_cast<int64_t>(m % a.C) * a.k;
-        for (int p = 0; p < a.k; ++p) {
-          copy_row(kc + (dst + p) * kslot, kc + (1 + p) * kslot, kw);
-          if (vc) copy_row(vc + (dst + p) * vslot, vc + (1 + p) * vslot, vw);
-        }
+        for (int p = 0; p < a.k; ++p)
+          copy_kv_row32(kc + (dst + p) * kslot, kc + (1 + p) * kslot, kw,
+                        vc ? vc + (dst + p) * vslot : nullptr, vc ? vc + (1 + p) * vslot : nullptr, vw, lane32);
       }
       const int64_t sdst = 1 + a.k + static_cast<int64_t>(a.C) * a.k + m;  // Fig. 4e
-      copy_row(kc + sdst * kslot, kn, kw);
-      if (vc) copy_row(vc + sdst * vslot, vn, vw);
+      copy_kv_row32(kc + sdst * kslot, kn, kw, vc ? vc + sdst * vslot : nullptr, vn, vw, lane32);
     }
   }
   __syncthreads();
@@ -122,16 +138,16 @@ __global__ void __launch_bounds__(256) cache_fill_kernel(CacheArgs a, int kw, in
   const int64_t rem = n_text - M * a.k;
   const int64_t L = n_text + M;
   const int64_t seq = static_cast<int64_t>(b) * a.hkv + h;
-  const int64_t slots_per_block = 8;
-  const int64_t s0 = static_cast<int64_t>(blockIdx.x) * slots_per_block;
   const int64_t nwrite = 1 + a.k + static_cast<int64_t>(a.C) * a.k + M;
-  for (int64_t slot = s0; slot < s0 + slots_per_block && slot < nwrite; ++slot) {
-    const int64_t row = fill_source_row(slot, M, rem, a.k, a.C);
-    if (row < 0) continue;
-    const int64_t src = (static_cast<int64_t>(b) * L + row) * a.hkv + h;
-    copy_row(ck + (seq * a.slots + slot) * kw, k_aug + src * kw, kw);
-    if (cv) copy_row(cv + (seq * a.slots + slot) * vw, v_aug + src * vw, vw);
-  }
+  // 8 slots per block, one 32-lane group each
+  const int64_t slot = static_cast<int64_t>(blockIdx.x) * 8 + (threadIdx.x >> 5);
+  if (slot >= nwrite) return;
+  const int64_t row = fill_source_row(slot, M, rem, a.k, a.C);
+  if (row < 0) return;
+  const int64_t src = (static_cast<int64_t>(b) * L + row) * a.hkv + h;
+  copy_kv_row32(ck + (seq * a.slots + slot) * kw, k_aug + src * kw, kw,
+                cv ? cv + (seq * a.slots + slot) * vw : nullptr, cv ? v_aug + src * vw : nullptr, vw,
+                threadIdx.x & 31);
 }
 
 __global__ void cache_fill_state_kernel(int32_t* state, int32_t batch, int64_t n_text, int32_t k) {
@@ -153,7 +169,7 @@ __global__ void cache_fill_state_kernel(int32_t* state, int32_t batch, int64_t n
 // summary slots m .. m + max_new_summaries - 1.  Ring positions whose
 // source is older than the segment were moved there by
 // cache_append_rows_commit_kernel, launched first.
-__global__ void __launch_bounds__(128) cache_append_rows_kernel(CacheArgs a, int kw, int vw,
+__global__ void __launch_bounds__(256) cache_append_rows_kernel(CacheArgs a, int kw, int vw,
                                                                 const int64_t* __restrict__ seg_rows,
                                                                 int64_t max_new_sum,
                                                                 uint32_t* __restrict__ ck,
@@ -171,16 +187,17 @@ __global__ void __launch_bounds__(128) cache_append_rows_kernel(CacheArgs a, int
   if (R <= 0 || m1 > a.max_summaries) return;
   const int64_t seq = static_cast<int64_t>(b) * a.hkv + h;
   const int64_t sum0 = 1 + a.k + static_cast<int64_t>(a.C) * a.k;
-  const int64_t s0 = static_cast<int64_t>(blockIdx.x) * 8;
-  for (int64_t e = s0; e < s0 + 8 && e < sum0 + max_new_sum; ++e) {
-    const int64_t slot = e < sum0 ? e : m + (e - sum0) + sum0;
-    if (e >= sum0 && slot >= sum0 + m1) break;
-    const int64_t row = fill_source_row(slot, m1, r1, a.k, a.C);
-    if (row < a0) continue;  // unchanged (or never written)
-    const int64_t src = (seg_rows[b] + row - a0) * a.hkv + h;
-    copy_row(ck + (seq * a.slots + slot) * kw, k_rows + src * kw, kw);
-    if (cv) copy_row(cv + (seq * a.slots + slot) * vw, v_rows + src * vw, vw);
-  }
+  // 8 slots per block, one 32-lane group each
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 8 + (threadIdx.x >> 5);
+  if (e >= sum0 + max_new_sum) return;
+  const int64_t slot = e < sum0 ? e : m + (e - sum0) + sum0;
+  if (e >= sum0 && slot >= sum0 + m1) return;
+  const int64_t row = fill_source_row(slot, m1, r1, a.k, a.C);
+  if (row < a0) return;  // unchanged (or never written)
+  const int64_t src = (seg_rows[b] + row - a0) * a.hkv + h;
+  copy_kv_row32(ck + (seq * a.slots + slot) * kw, k_rows + src * kw, kw,
+                cv ? cv + (seq * a.slots + slot) * vw : nullptr, cv ? v_rows + src * vw : nullptr, vw,
+                threadIdx.x & 31);
 }
 
 // Runs before cache_append_rows_kernel: when the segment completes chunk m,
@@ -188,7 +205,7 @@ __global__ void __launch_bounds__(128) cache_append_rows_kernel(CacheArgs a, int
 // go to ring chunk slot m mod C (position k - 1 - o), as the summary
 // append's block copy would move them (Fig. 4d); the main kernel may then
 // overwrite the current chunk with later tokens.
-__global__ void __launch_bounds__(128) cache_append_rows_commit_kernel(CacheArgs a, int kw, int vw,
+__global__ void __launch_bounds__(256) cache_append_rows_commit_kernel(CacheArgs a, int kw, int vw,
                                                                        const int64_t* __restrict__ seg_rows,
                                                                        uint32_t* __restrict__ ck,
                                                                        uint32_t* __restrict__ cv,
@@ -201,10 +218,10 @@ __global__ void __launch_bounds__(128) cache_append_rows_commit_kernel(CacheArgs
   if (a.C == 0 || m1 <= m || m1 > a.max_summaries) return;
   const int64_t seq = static_cast<int64_t>(b) * a.hkv + h;
   const int64_t dst = 1 + a.k + (m % a.C) * a.k;
-  for (int64_t o = 0; o < r && o < a.k; ++o) {
-    copy_row(ck + (seq * a.slots + dst + a.k - 1 - o) * kw, ck + (seq * a.slots + a.k - o) * kw, kw);
-    if (cv) copy_row(cv + (seq * a.slots + dst + a.k - 1 - o) * vw, cv + (seq * a.slots + a.k - o) * vw, vw);
-  }
+  for (int64_t o = threadIdx.x >> 5; o < r && o < a.k; o += blockDim.x >> 5)
+    copy_kv_row32(ck + (seq * a.slots + dst + a.k - 1 - o) * kw, ck + (seq * a.slots + a.k - o) * kw, kw,
+                  cv ? cv + (seq * a.slots + dst + a.k - 1 - o) * vw : nullptr,
+                  cv ? cv + (seq * a.slots + a.k - o) * vw : nullptr, vw, threadIdx.x & 31);
 }
 
 // New state {m', r'} (or the overflow error) once every copy is done.
@@ -254,12 +271,12 @@ hipError_t launch_cache_append_rows(const CacheArgs& a, int32_t dtype, const int
   const bool has_v = !a.v_is_k_prefix;
   const int64_t max_new_sum = max_rows / (a.k + 1) + 1;
   const int64_t n = 1 + a.k + static_cast<int64_t>(a.C) * a.k + max_new_sum;
-  hipLaunchKernelGGL(cache_append_rows_commit_kernel, dim3(1, a.hkv, a.batch), dim3(128), 0, s, a, kw, vw, seg_rows,
+  hipLaunchKernelGGL(cache_append_rows_commit_kernel, dim3(1, a.hkv, a.batch), dim3(256), 0, s, a, kw, vw, seg_rows,
                      static_cast<uint32_t*>(ck), has_v ? static_cast<uint32_t*>(cv) : nullptr, state);
   hipError_t e0 = hipGetLastError();
   if (e0 != hipSuccess) return e0;
   hipLaunchKernelGGL(cache_append_rows_kernel, dim3(static_cast<uint32_t>((n + 7) / 8), a.hkv, a.batch),
-                     dim3(128), 0, s, a, kw, vw, seg_rows, max_new_sum, static_cast<uint32_t*>(ck),
+                     dim3(256), 0, s, a, kw, vw, seg_rows, max_new_sum, static_cast<uint32_t*>(ck),
                      has_v ? static_cast<uint32_t*>(cv) : nullptr, state, static_cast<const uint32_t*>(k_rows),
                      has_v ? static_cast<const uint32_t*>(v_rows) : nullptr);
   hipError_t e = hipGetLastError();
@@ -277,7 +294,7 @@ hipError_t launch_cache_fill(const CacheArgs& a, int32_t dtype, int64_t n_text, 
   const int64_t M = n_text / a.k;
   const int64_t nwrite = 1 + a.k + static_cast<int64_t>(a.C) * a.k + M;
   const int64_t gx = (nwrite + 7) / 8;
-  hipLaunchKernelGGL(cache_fill_kernel, dim3(static_cast<uint32_t>(gx), a.hkv, a.batch), dim3(128),
+  hipLaunchKernelGGL(cache_fill_kernel, dim3(static_cast<uint32_t>(gx), a.hkv, a.batch), dim3(256),
                      0, s, a, kw, vw, n_text, static_cast<uint32_t*>(ck),
                      has_v ? static_cast<uint32_t*>(cv) : nullptr,
                      static_cast<const uint32_t*>(k_aug),
