@@ -21,8 +21,7 @@ reordering beyond what the definitions state:
 * attention backward ............ chain rule through Eq. (10) (the report
   trains with this kernel, Sec. 2.3); the softmax Jacobian written out
 
-Readings taken where the pages are silent or ambiguous (each one is listed,
-with its reason, in the design notes at the repository root):
+Readings taken where the pages are silent or ambiguous:
 
 * a summary token sees the k text tokens of its own chunk and itself
   (``summary_sees_self=True``, the default); the other reading (k keys) is
