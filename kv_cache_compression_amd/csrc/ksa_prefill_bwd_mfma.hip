@@ -561,16 +561,16 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_d128_kernel(
     // registers within two waves per SIMD)
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-      f32x16_t s, dp;
+      // S first, turned into P (kept in fp32 only until packed to bf16),
+      // then dP: the two score blocks are never live together
+      f32x16_t s;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+      for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
         const int off = (qoff0 ^ (ks << 5)) + 32 * ROW_BYTES * blk;
-        const bf16x8_t qa_ = *reinterpret_cast<const bf16x8_t*>(ql + off);
-        const bf16x8_t ga_ = *reinterpret_cast<const bf16x8_t*>(gl + off);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa_, kop[ks], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga_, vop[ks], dp, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t*>(ql + off), kop[ks], s, 0, 0,
+                                                    0);
       }
       // visibility of (query row 32 blk + 8 (r / 4) + 4 half + r % 4, lane's key)
       if (!full) {
@@ -580,23 +580,35 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_d128_kernel(
           s[r] = (off >= lo && off <= hi) ? s[r] : kNegInf;
         }
       }
+      float p[16];
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(st + 32 * blk + 8 * r4 + 4 * half);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[4 * r4 + e] = fast_exp2(s[4 * r4 + e] * a.sl - l4[e]);
+      }
+      f32x16_t dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dp[r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const int off = (qoff0 ^ (ks << 5)) + 32 * ROW_BYTES * blk;
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t*>(gl + off), vop[ks], dp, 0, 0,
+                                                     0);
+      }
       u32x4_t pw[2], dw[2];
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int row = 32 * blk + 8 * r4 + 4 * half;
-        const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(st + row);
         const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(st + BN + row);
-        float p[4], ds[4];
+        float ds[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          p[e] = fast_exp2(s[4 * r4 + e] * a.sl - l4[e]);
-          ds[e] = p[e] * (dp[4 * r4 + e] - d4[e]);
-        }
+        for (int e = 0; e < 4; ++e) ds[e] = p[4 * r4 + e] * (dp[4 * r4 + e] - d4[e]);
         // query k-slots of step 2 blk + r4 / 2: rows 16 ks + 4 half + {0..3}, +8
         const int kk = r4 >> 1;
         const int w0 = 2 * (r4 & 1);
-        pw[kk][w0] = pk_bf16(p[0], p[1]);
-        pw[kk][w0 + 1] = pk_bf16(p[2], p[3]);
+        pw[kk][w0] = pk_bf16(p[4 * r4 + 0], p[4 * r4 + 1]);
+        pw[kk][w0 + 1] = pk_bf16(p[4 * r4 + 2], p[4 * r4 + 3]);
         dw[kk][w0] = pk_bf16(ds[0], ds[1]);
         dw[kk][w0 + 1] = pk_bf16(ds[2], ds[3]);
       }
