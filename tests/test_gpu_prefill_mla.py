@@ -70,3 +70,28 @@ def test_mla_prefill_values(n, k, C, batch):
         el = np.abs(_np(lse[b]) - rl)
         print(f"  b{b}: max {e.max():.3e} mean {e.mean():.3e} lse {el.max():.3e}", flush=True)
         assert e.max() <= 2e-2 and e.mean() <= 2e-3 and el.max() <= 2e-2
+
+
+def test_mla_prefill_late_large_scores():
+    """The 64 rotary key columns (not part of V) of the second half of the
+    sequence are 300x larger, so for half of the rows a later key tile's
+    maximum exceeds the first tile's by more than 2^127: exponentials taken
+    against the first tile's maximum would overflow, and those rows must take
+    the second pass with the row's own maximum.  Values and normalisers
+    against the oracle."""
+    dev = _dev()
+    n, k, C = 400, 8, 3
+    L = O.augmented_len(n, k)
+    g = ksa_synth.gen(77)
+    q = ksa_synth.normal((1, L, HQ, DQK), torch.bfloat16, g)
+    kx = ksa_synth.normal((1, L, 1, DQK), torch.bfloat16, g)
+    kx[:, L // 2:, :, DV:] = (kx[:, L // 2:, :, DV:].float() * 300).to(torch.bfloat16)
+    p = ksa.Params(k, C, HQ, 1, DQK, DV, torch.bfloat16, v_is_k_prefix=True)
+    lse = torch.empty((1, HQ, L), dtype=torch.float32, device=dev)
+    out = ksa.ksa_prefill_attn(p, q.to(dev), kx.to(dev), None, n, lse=lse)
+    torch.cuda.synchronize()
+    ref, rl = O.ksa_attention(q[0].double().numpy(), kx[0].double().numpy(), None, n, k, C, p.scale, dv=DV)
+    e = np.abs(_np(out[0]) - ref)
+    el = np.abs(_np(lse[0]) - rl)
+    print(f"late large scores: max {e.max():.3e} mean {e.mean():.3e} lse {el.max():.3e}", flush=True)
+    assert e.max() <= 2e-2 and e.mean() <= 2e-3 and el.max() <= 2e-2
