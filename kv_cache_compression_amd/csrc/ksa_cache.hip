@@ -166,15 +166,24 @@ __global__ void cache_fill_state_kernel(int32_t* state, int32_t batch, int64_t n
 // a0 + R rows, i.e. state m' = a1 / (k+1), r' = a1 % (k+1); a slot whose
 // source row under that state is a new row (>= a0) takes it, every other
 // slot keeps its contents.  Grid x covers scratch, current, ring and the
-// summary slots m .. m + max_new_summaries - 1.  Ring positions whose
-// source is older than the segment were moved there by
-// cache_append_rows_commit_kernel, launched first.
+// summary slots m .. m + max_new_summaries - 1, one 32-lane group per slot.
+//
+// When the segment completes chunk m, its tokens that arrived before the
+// segment (current slots k - o, o < r) belong in ring chunk slot m mod C at
+// position k - 1 - o, as the summary append's block copy would move them
+// (Fig. 4d), unless a later chunk of the segment lands there too.  The group
+// of current slot k - o moves that token before it writes the slot's new
+// contents, so no other group reads or writes either slot.
+//
+// The last block of a sequence to finish (a counter in the state's spare
+// word) writes the new state {m', r'}; every block has read the old state
+// before it counts itself.
 __global__ void __launch_bounds__(256) cache_append_rows_kernel(CacheArgs a, int kw, int vw,
                                                                 const int64_t* __restrict__ seg_rows,
                                                                 int64_t max_new_sum,
                                                                 uint32_t* __restrict__ ck,
                                                                 uint32_t* __restrict__ cv,
-                                                                const int32_t* __restrict__ state,
+                                                                int32_t* __restrict__ state,
                                                                 const uint32_t* __restrict__ k_rows,
                                                                 const uint32_t* __restrict__ v_rows) {
   const int h = blockIdx.y;
@@ -184,60 +193,42 @@ __global__ void __launch_bounds__(256) cache_append_rows_kernel(CacheArgs a, int
   const int64_t R = seg_rows[b + 1] - seg_rows[b];
   const int64_t a1 = a0 + R;
   const int64_t m1 = a1 / (a.k + 1), r1 = a1 - m1 * (a.k + 1);
-  if (R <= 0 || m1 > a.max_summaries) return;
-  const int64_t seq = static_cast<int64_t>(b) * a.hkv + h;
-  const int64_t sum0 = 1 + a.k + static_cast<int64_t>(a.C) * a.k;
-  // 8 slots per block, one 32-lane group each
-  const int64_t e = static_cast<int64_t>(blockIdx.x) * 8 + (threadIdx.x >> 5);
-  if (e >= sum0 + max_new_sum) return;
-  const int64_t slot = e < sum0 ? e : m + (e - sum0) + sum0;
-  if (e >= sum0 && slot >= sum0 + m1) return;
-  const int64_t row = fill_source_row(slot, m1, r1, a.k, a.C);
-  if (row < a0) return;  // unchanged (or never written)
-  const int64_t src = (seg_rows[b] + row - a0) * a.hkv + h;
-  copy_kv_row32(ck + (seq * a.slots + slot) * kw, k_rows + src * kw, kw,
-                cv ? cv + (seq * a.slots + slot) * vw : nullptr, cv ? v_rows + src * vw : nullptr, vw,
-                threadIdx.x & 31);
-}
-
-// Runs before cache_append_rows_kernel: when the segment completes chunk m,
-// the tokens of chunk m that arrived before it (current slots k - o, o < r)
-// go to ring chunk slot m mod C (position k - 1 - o), as the summary
-// append's block copy would move them (Fig. 4d); the main kernel may then
-// overwrite the current chunk with later tokens.
-__global__ void __launch_bounds__(256) cache_append_rows_commit_kernel(CacheArgs a, int kw, int vw,
-                                                                       const int64_t* __restrict__ seg_rows,
-                                                                       uint32_t* __restrict__ ck,
-                                                                       uint32_t* __restrict__ cv,
-                                                                       const int32_t* __restrict__ state) {
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
-  const int64_t m = state[4 * b + 0], r = state[4 * b + 1];
-  const int64_t a1 = m * (a.k + 1) + r + seg_rows[b + 1] - seg_rows[b];
-  const int64_t m1 = a1 / (a.k + 1);
-  if (a.C == 0 || m1 <= m || m1 > a.max_summaries) return;
-  const int64_t seq = static_cast<int64_t>(b) * a.hkv + h;
-  const int64_t dst = 1 + a.k + (m % a.C) * a.k;
-  for (int64_t o = threadIdx.x >> 5; o < r && o < a.k; o += blockDim.x >> 5)
-    copy_kv_row32(ck + (seq * a.slots + dst + a.k - 1 - o) * kw, ck + (seq * a.slots + a.k - o) * kw, kw,
-                  cv ? cv + (seq * a.slots + dst + a.k - 1 - o) * vw : nullptr,
-                  cv ? cv + (seq * a.slots + a.k - o) * vw : nullptr, vw, threadIdx.x & 31);
-}
-
-// New state {m', r'} (or the overflow error) once every copy is done.
-__global__ void cache_append_rows_state_kernel(int32_t* state, int32_t batch, const int64_t* seg_rows,
-                                               int32_t k, int32_t max_summaries) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= batch) return;
-  const int64_t a1 = static_cast<int64_t>(state[4 * b]) * (k + 1) + state[4 * b + 1] + seg_rows[b + 1] -
-                     seg_rows[b];
-  const int64_t m1 = a1 / (k + 1);
-  if (m1 > max_summaries) {
-    state[4 * b + 3] |= KSA_CACHE_ERR_SUMMARY_FULL;
+  if (R <= 0) return;  // uniform over the sequence's blocks: state unchanged
+  if (m1 > a.max_summaries) {
+    if (blockIdx.x == 0 && h == 0 && threadIdx.x == 0) state[4 * b + 3] |= KSA_CACHE_ERR_SUMMARY_FULL;
     return;
   }
-  state[4 * b + 0] = static_cast<int32_t>(m1);
-  state[4 * b + 1] = static_cast<int32_t>(a1 - m1 * (k + 1));
+  const int64_t seq = static_cast<int64_t>(b) * a.hkv + h;
+  const int64_t sum0 = 1 + a.k + static_cast<int64_t>(a.C) * a.k;
+  const int lane32 = threadIdx.x & 31;
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 8 + (threadIdx.x >> 5);
+  const int64_t slot = e < sum0 ? e : m + (e - sum0) + sum0;
+  if (e < sum0 + max_new_sum && !(e >= sum0 && slot >= sum0 + m1)) {
+    // the pre-segment token of the completed chunk that sits in this current slot
+    if (slot >= 1 && slot <= a.k && a.C > 0 && m1 > m) {
+      const int64_t o = a.k - slot;
+      const int64_t ring = 1 + a.k + (m % a.C) * a.k + a.k - 1 - o;
+      if (o < r && fill_source_row(ring, m1, r1, a.k, a.C) < a0)
+        copy_kv_row32(ck + (seq * a.slots + ring) * kw, ck + (seq * a.slots + slot) * kw, kw,
+                      cv ? cv + (seq * a.slots + ring) * vw : nullptr, cv ? cv + (seq * a.slots + slot) * vw : nullptr,
+                      vw, lane32);
+    }
+    const int64_t row = fill_source_row(slot, m1, r1, a.k, a.C);
+    if (row >= a0) {  // otherwise unchanged (or never written)
+      const int64_t src = (seg_rows[b] + row - a0) * a.hkv + h;
+      copy_kv_row32(ck + (seq * a.slots + slot) * kw, k_rows + src * kw, kw,
+                    cv ? cv + (seq * a.slots + slot) * vw : nullptr, cv ? v_rows + src * vw : nullptr, vw, lane32);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int total = static_cast<int>(gridDim.x * gridDim.y);
+    if (atomicAdd(&state[4 * b + 2], 1) == total - 1) {
+      state[4 * b + 0] = static_cast<int32_t>(m1);
+      state[4 * b + 1] = static_cast<int32_t>(r1);
+      state[4 * b + 2] = 0;
+    }
+  }
 }
 
 static int words_per_row(int d, int32_t dtype) {
@@ -271,18 +262,10 @@ hipError_t launch_cache_append_rows(const CacheArgs& a, int32_t dtype, const int
   const bool has_v = !a.v_is_k_prefix;
   const int64_t max_new_sum = max_rows / (a.k + 1) + 1;
   const int64_t n = 1 + a.k + static_cast<int64_t>(a.C) * a.k + max_new_sum;
-  hipLaunchKernelGGL(cache_append_rows_commit_kernel, dim3(1, a.hkv, a.batch), dim3(256), 0, s, a, kw, vw, seg_rows,
-                     static_cast<uint32_t*>(ck), has_v ? static_cast<uint32_t*>(cv) : nullptr, state);
-  hipError_t e0 = hipGetLastError();
-  if (e0 != hipSuccess) return e0;
   hipLaunchKernelGGL(cache_append_rows_kernel, dim3(static_cast<uint32_t>((n + 7) / 8), a.hkv, a.batch),
                      dim3(256), 0, s, a, kw, vw, seg_rows, max_new_sum, static_cast<uint32_t*>(ck),
                      has_v ? static_cast<uint32_t*>(cv) : nullptr, state, static_cast<const uint32_t*>(k_rows),
                      has_v ? static_cast<const uint32_t*>(v_rows) : nullptr);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(cache_append_rows_state_kernel, dim3((a.batch + 255) / 256), dim3(256), 0, s, state, a.batch,
-                     seg_rows, a.k, a.max_summaries);
   return hipGetLastError();
 }
 
