@@ -2,6 +2,7 @@
 prefill, in the launch configuration it times them, on sampled rows the
 oracle computes one by one:
 
+  - the RoPE pre-pass of the 32768-token workload;
   - the 32768-token, 32/8-head workload fed through the cache in 8 segments
     (ksa_prefill_chunk + ksa_cache_append_rows per segment);
   - the same workload under the two summary-free baselines (sliding chunks,
@@ -63,6 +64,16 @@ def w32k():
                bounds=bounds)
     del qd, kd, vd
     torch.cuda.empty_cache()
+
+
+def test_rope_pre_pass_32k_sampled_rows(w32k):
+    """The RoPE pre-pass over the 32K augmented Q and K (position ids of the
+    summary rows included) against the oracle's rotation, on sampled rows."""
+    rows = w32k["rows"]
+    for name, got, ref in (("q", w32k["qd"], w32k["q"]), ("k", w32k["kd"], w32k["k"])):
+        e = np.abs(got[0, rows].float().cpu().double().numpy() - ref[rows])
+        print(f"rope {name}: max {e.max():.3e} mean {e.mean():.3e}", flush=True)
+        assert e.max() <= 2e-2 and e.mean() <= 2e-3, (name, e.max(), e.mean())
 
 
 def test_chunked_32k_in_8_segments_sampled_rows(w32k):
