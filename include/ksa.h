@@ -86,9 +86,8 @@ typedef struct {
  *   slots k+1 .. k+C*k           sliding-chunk ring, chunk j in ring slot j mod C (Fig. 4d)
  *   slots k+1+C*k ..             summary buffer, s_0, s_1, ... (Fig. 4e)
  * state[b*4 + 0] = m, committed chunks; state[b*4 + 1] = r, tokens in the
- * current chunk (0..k); state[b*4 + 2] is 0 between calls (reset and fill
- * set it; ksa_cache_append_rows counts its finished blocks there and leaves
- * it 0); state[b*4 + 3] = error bits (KSA_CACHE_ERR_*).  Keys are stored
+ * current chunk (0..k); state[b*4 + 2] reserved (0); state[b*4 + 3] =
+ * error bits (KSA_CACHE_ERR_*).  Keys are stored
  * after RoPE. */
 typedef struct {
   void* k;               /* [batch, Hkv, slots, Dqk] */

@@ -175,9 +175,8 @@ __global__ void cache_fill_state_kernel(int32_t* state, int32_t batch, int64_t n
 // of current slot k - o moves that token before it writes the slot's new
 // contents, so no other group reads or writes either slot.
 //
-// The last block of a sequence to finish (a counter in the state's spare
-// word) writes the new state {m', r'}; every block has read the old state
-// before it counts itself.
+// The new state {m', r'} is written by a second, one-thread-per-sequence
+// kernel once every block has read the old one.
 __global__ void __launch_bounds__(256) cache_append_rows_kernel(CacheArgs a, int kw, int vw,
                                                                 const int64_t* __restrict__ seg_rows,
                                                                 int64_t max_new_sum,
@@ -194,10 +193,7 @@ __global__ void __launch_bounds__(256) cache_append_rows_kernel(CacheArgs a, int
   const int64_t a1 = a0 + R;
   const int64_t m1 = a1 / (a.k + 1), r1 = a1 - m1 * (a.k + 1);
   if (R <= 0) return;  // uniform over the sequence's blocks: state unchanged
-  if (m1 > a.max_summaries) {
-    if (blockIdx.x == 0 && h == 0 && threadIdx.x == 0) state[4 * b + 3] |= KSA_CACHE_ERR_SUMMARY_FULL;
-    return;
-  }
+  if (m1 > a.max_summaries) return;  // flagged by the state kernel; the cache is left as it was
   const int64_t seq = static_cast<int64_t>(b) * a.hkv + h;
   const int64_t sum0 = 1 + a.k + static_cast<int64_t>(a.C) * a.k;
   const int lane32 = threadIdx.x & 31;
@@ -220,15 +216,21 @@ __global__ void __launch_bounds__(256) cache_append_rows_kernel(CacheArgs a, int
                     cv ? cv + (seq * a.slots + slot) * vw : nullptr, cv ? v_rows + src * vw : nullptr, vw, lane32);
     }
   }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int total = static_cast<int>(gridDim.x * gridDim.y);
-    if (atomicAdd(&state[4 * b + 2], 1) == total - 1) {
-      state[4 * b + 0] = static_cast<int32_t>(m1);
-      state[4 * b + 1] = static_cast<int32_t>(r1);
-      state[4 * b + 2] = 0;
-    }
+}
+
+__global__ void cache_append_rows_state_kernel(int32_t* state, int32_t batch, const int64_t* seg_rows,
+                                               int32_t k, int32_t max_summaries) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= batch) return;
+  const int64_t a1 = static_cast<int64_t>(state[4 * b]) * (k + 1) + state[4 * b + 1] + seg_rows[b + 1] -
+                     seg_rows[b];
+  const int64_t m1 = a1 / (k + 1);
+  if (m1 > max_summaries) {
+    state[4 * b + 3] |= KSA_CACHE_ERR_SUMMARY_FULL;
+    return;
   }
+  state[4 * b + 0] = static_cast<int32_t>(m1);
+  state[4 * b + 1] = static_cast<int32_t>(a1 - m1 * (k + 1));
 }
 
 static int words_per_row(int d, int32_t dtype) {
@@ -266,6 +268,10 @@ hipError_t launch_cache_append_rows(const CacheArgs& a, int32_t dtype, const int
                      dim3(256), 0, s, a, kw, vw, seg_rows, max_new_sum, static_cast<uint32_t*>(ck),
                      has_v ? static_cast<uint32_t*>(cv) : nullptr, state, static_cast<const uint32_t*>(k_rows),
                      has_v ? static_cast<const uint32_t*>(v_rows) : nullptr);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(cache_append_rows_state_kernel, dim3((a.batch + 255) / 256), dim3(256), 0, s, state, a.batch,
+                     seg_rows, a.k, a.max_summaries);
   return hipGetLastError();
 }
 

@@ -79,7 +79,7 @@ def test_append_rows_matches_slot_model(k, C, dtype, D):
         for b in range(3):
             mdl = models[b]
             assert st[b, 0].item() == mdl.m and st[b, 1].item() == mdl.r and st[b, 3].item() == 0
-            assert st[b, 2].item() == 0   # the completion counter is left at 0
+            assert st[b, 2].item() == 0   # reserved word untouched
             want = torch.tensor([0.0 if t is None else float(t) for t in mdl.slots])
             assert torch.equal(ck[b, :, :, 0], want[None].expand(hkv, -1))
             assert torch.equal(cv[b, :, :, 0], -want[None].expand(hkv, -1))
