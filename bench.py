@@ -477,7 +477,7 @@ def prefill_backward(ksa, ksa_synth, torch, w, p, qd, kd, vd, stream, reps: int 
             "workspace_mb": round(ksa.ksa_prefill_bwd_workspace_bytes(p, w.batch, w.n_text) / 1e6, 1)}
 
 
-def prefill_chunked(ksa, torch, w, p, qd, kd, vd, stream, n_chunks: int = 8, reps: int = 3) -> dict:
+def prefill_chunked(ksa, torch, w, p, qd, kd, vd, stream, n_chunks: int = 8, reps: int = 10) -> dict:
     """The same workload fed in n_chunks segments through the cache: each
     segment is prefilled against the cache (ksa_prefill_chunk) and then
     appended (ksa_cache_append_rows); one pass = the whole sequence."""
