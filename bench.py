@@ -202,7 +202,7 @@ def main() -> int:
         ksa.ksa_decode_attn(mc, mq, mkind, out=mout, workspace=mws, stream=stream)
         ev[6].record(stream)
 
-    # the box's own ceilings, measured before the timed work so that they are
+    # the GPU's own ceilings, measured before the timed work so that they are
     # not taken on a chip already heated by it
     peaks = machine_peaks(torch, dev, stream)
 

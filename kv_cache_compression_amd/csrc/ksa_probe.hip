@@ -10,7 +10,7 @@
 //   - a streaming HBM read (16-byte non-temporal loads, eight in flight per
 //     thread), the access pattern of the split-K decode;
 //   - a streaming HBM copy (16-byte loads and stores).
-// None of these is part of the attention path; they only measure the box.
+// None of these is part of the attention path; they only measure the GPU.
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
