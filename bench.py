@@ -370,8 +370,8 @@ def copy_probe() -> int:
 
 def prefill_traffic():
     """HBM bytes per prefill launch from the committed counter summary, or
-    None when the summary is missing or the kernel source has changed since
-    the counters were taken."""
+    None when the summary is missing or the kernel source (or its extra
+    compile flags) has changed since the counters were taken."""
     import hashlib
 
     try:
@@ -381,8 +381,11 @@ def prefill_traffic():
                 if "=" in line and not line.lstrip().startswith("#"):
                     key, val = line.split("=", 1)
                     kv[key.strip()] = val.strip()
-        with open(PREFILL_SOURCE, "rb") as f:
-            digest = hashlib.sha256(f.read()).hexdigest()
+        from kv_cache_compression_amd import _build as kb
+
+        flags = " ".join(kb.EXTRA.get(os.path.basename(PREFILL_SOURCE), [])).encode()
+        with open(PREFILL_SOURCE, "rb") as f:   # the source and its extra compile flags
+            digest = hashlib.sha256(f.read() + flags).hexdigest()
         if kv.get("kernel_source_sha256") != digest:
             return None
         fetch = float(kv["fetch_kib_per_dispatch"]) * float(kv["fetch_scale"]) * 1024

@@ -37,6 +37,12 @@ COMMON = [
     "-Wno-unused-command-line-argument",
 ]
 
+# Per-file extra flags.  The one-shot prefill is scheduled for instruction-
+# level parallelism (same code and results, 0.5-1.7% faster at 32K and 128K).
+EXTRA = {
+    "ksa_prefill_mfma.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+}
+
 
 def hipcc() -> str:
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
@@ -48,7 +54,7 @@ def hipcc() -> str:
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [hipcc()] + COMMON + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + COMMON + EXTRA.get(src, []) + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
