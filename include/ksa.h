@@ -100,7 +100,10 @@ enum {
   KSA_CACHE_ERR_CHUNK_FULL = 1,      /* text append with r == k */
   KSA_CACHE_ERR_CHUNK_NOT_FULL = 2,  /* summary append with r != k */
   KSA_CACHE_ERR_SUMMARY_FULL = 4,    /* summary append with m == max_summaries */
-  KSA_CACHE_ERR_BAD_SUMMARY_READ = 8 /* summary decode without a just-committed chunk */
+  KSA_CACHE_ERR_BAD_SUMMARY_READ = 8, /* summary decode without a just-committed chunk */
+  KSA_CACHE_ERR_BAD_SEGMENT = 16      /* row-wise append or chunked prefill whose segment
+                                         length is negative or above max_rows, or whose
+                                         state {m, r} is out of range */
 };
 
 KSA_API const char* ksa_status_string(int32_t status);
@@ -197,9 +200,12 @@ KSA_API int32_t ksa_cache_reset(const ksa_params* p, const ksa_cache* c, int32_t
 KSA_API int32_t ksa_cache_append(const ksa_params* p, const ksa_cache* c, int32_t batch, const void* k_new,
                          const void* v_new, const int32_t* kind, void* stream);
 
-/* Bulk hand-off from prefill: the result equals appending the L augmented
- * rows one by one (text rows as kind 0, summary rows as kind 1), starting
- * from an empty cache, for every sequence.
+/* Bulk hand-off from prefill to decode (Sec. 2.3.1: the cache that decoding
+ * reads holds the keys and values the prefill produced, in the regions of
+ * Fig. 4a): the result equals appending the L augmented rows one by one
+ * (text rows as kind 0, summary rows as kind 1, Fig. 4b-4e), starting from
+ * an empty cache, for every sequence.  Slots that those appends would never
+ * write are left as they were.
  *   k_aug [batch, L, Hkv, Dqk], v_aug [batch, L, Hkv, Dv] (post-RoPE). */
 KSA_API int32_t ksa_cache_fill(const ksa_params* p, const ksa_cache* c, int32_t batch, int64_t n_text,
                        const void* k_aug, const void* v_aug, void* stream);
@@ -213,7 +219,10 @@ KSA_API int32_t ksa_cache_fill(const ksa_params* p, const ksa_cache* c, int32_t 
  *   k_rows [seg_rows[batch], Hkv, Dqk], v_rows [.., Hkv, Dv] (post-RoPE)
  *   max_rows >= every R_b (sizes the launch).
  * A sequence whose summaries would exceed max_summaries is left untouched
- * and gets KSA_CACHE_ERR_SUMMARY_FULL. */
+ * and gets KSA_CACHE_ERR_SUMMARY_FULL; one whose R_b is negative or above
+ * max_rows, or whose state is out of range (r outside 0..k, m outside
+ * 0..max_summaries), is left untouched and gets KSA_CACHE_ERR_BAD_SEGMENT.
+ * R_b = 0 is a no-op. */
 KSA_API int32_t ksa_cache_append_rows(const ksa_params* p, const ksa_cache* c, int32_t batch,
                               const int64_t* seg_rows, int64_t max_rows, const void* k_rows,
                               const void* v_rows, void* stream);
@@ -231,9 +240,12 @@ KSA_API int32_t ksa_cache_append_rows(const ksa_params* p, const ksa_cache* c, i
  *   q   [total_rows, Hq, Dqk]   k [total_rows, Hkv, Dqk]   v [total_rows, Hkv, Dv]
  *   out [total_rows, Hq, Dv]    lse [Hq, total_rows] fp32 natural log, or NULL
  *   max_rows >= every R_b, total_rows = seg_rows[batch].
- * The cache is read only; ksa_cache_append_rows with the same seg_rows and
- * k / v then moves the segment into it.  A sequence whose cache state is out
- * of range (m > max_summaries, r > k) is skipped: its rows are not written. */
+ * The cache regions are read only; ksa_cache_append_rows with the same
+ * seg_rows and k / v then moves the segment into it.  A sequence whose cache
+ * state is out of range (m > max_summaries, r > k) or whose R_b is negative
+ * or above max_rows is skipped (its rows are not written) and gets
+ * KSA_CACHE_ERR_BAD_SEGMENT in its state's error word, the only state word
+ * this call may write. */
 KSA_API int32_t ksa_prefill_chunk(const ksa_params* p, const ksa_cache* c, int32_t batch,
                           const int64_t* seg_rows, int64_t max_rows, int64_t total_rows, const void* q,
                           const void* k, const void* v, void* out, float* lse, void* stream);

@@ -29,6 +29,7 @@ KSA_CACHE_ERR_CHUNK_FULL = 1
 KSA_CACHE_ERR_CHUNK_NOT_FULL = 2
 KSA_CACHE_ERR_SUMMARY_FULL = 4
 KSA_CACHE_ERR_BAD_SUMMARY_READ = 8
+KSA_CACHE_ERR_BAD_SEGMENT = 16
 
 # Every symbol the header declares.
 EXPORTS = (

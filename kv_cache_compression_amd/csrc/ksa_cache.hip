@@ -176,10 +176,18 @@ __global__ void cache_fill_state_kernel(int32_t* state, int32_t batch, int64_t n
 // contents, so no other group reads or writes either slot.
 //
 // The new state {m', r'} is written by a second, one-thread-per-sequence
-// kernel once every block has read the old one.
+// kernel once every block has read the old one.  A segment longer than
+// max_rows (the launch covers only max_new_sum summary slots), a negative
+// one or a state out of range leaves the sequence untouched; the state
+// kernel flags it.
+__device__ __forceinline__ bool append_rows_ok(const CacheArgs& a, int64_t m, int64_t r, int64_t R,
+                                               int64_t max_rows) {
+  return R >= 0 && R <= max_rows && m >= 0 && m <= a.max_summaries && r >= 0 && r <= a.k;
+}
+
 __global__ void __launch_bounds__(256) cache_append_rows_kernel(CacheArgs a, int kw, int vw,
                                                                 const int64_t* __restrict__ seg_rows,
-                                                                int64_t max_new_sum,
+                                                                int64_t max_rows, int64_t max_new_sum,
                                                                 uint32_t* __restrict__ ck,
                                                                 uint32_t* __restrict__ cv,
                                                                 int32_t* __restrict__ state,
@@ -192,7 +200,7 @@ __global__ void __launch_bounds__(256) cache_append_rows_kernel(CacheArgs a, int
   const int64_t R = seg_rows[b + 1] - seg_rows[b];
   const int64_t a1 = a0 + R;
   const int64_t m1 = a1 / (a.k + 1), r1 = a1 - m1 * (a.k + 1);
-  if (R <= 0) return;  // uniform over the sequence's blocks: state unchanged
+  if (R == 0 || !append_rows_ok(a, m, r, R, max_rows)) return;  // uniform over the sequence's blocks
   if (m1 > a.max_summaries) return;  // flagged by the state kernel; the cache is left as it was
   const int64_t seq = static_cast<int64_t>(b) * a.hkv + h;
   const int64_t sum0 = 1 + a.k + static_cast<int64_t>(a.C) * a.k;
@@ -218,12 +226,18 @@ __global__ void __launch_bounds__(256) cache_append_rows_kernel(CacheArgs a, int
   }
 }
 
-__global__ void cache_append_rows_state_kernel(int32_t* state, int32_t batch, const int64_t* seg_rows,
-                                               int32_t k, int32_t max_summaries) {
+__global__ void cache_append_rows_state_kernel(CacheArgs a, int32_t* state, const int64_t* seg_rows,
+                                               int64_t max_rows) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= batch) return;
-  const int64_t a1 = static_cast<int64_t>(state[4 * b]) * (k + 1) + state[4 * b + 1] + seg_rows[b + 1] -
-                     seg_rows[b];
+  if (b >= a.batch) return;
+  const int32_t k = a.k, max_summaries = a.max_summaries;
+  const int64_t m = state[4 * b], r = state[4 * b + 1];
+  const int64_t R = seg_rows[b + 1] - seg_rows[b];
+  if (!append_rows_ok(a, m, r, R, max_rows)) {
+    state[4 * b + 3] |= KSA_CACHE_ERR_BAD_SEGMENT;
+    return;
+  }
+  const int64_t a1 = m * (k + 1) + r + R;
   const int64_t m1 = a1 / (k + 1);
   if (m1 > max_summaries) {
     state[4 * b + 3] |= KSA_CACHE_ERR_SUMMARY_FULL;
@@ -265,13 +279,13 @@ hipError_t launch_cache_append_rows(const CacheArgs& a, int32_t dtype, const int
   const int64_t max_new_sum = max_rows / (a.k + 1) + 1;
   const int64_t n = 1 + a.k + static_cast<int64_t>(a.C) * a.k + max_new_sum;
   hipLaunchKernelGGL(cache_append_rows_kernel, dim3(static_cast<uint32_t>((n + 7) / 8), a.hkv, a.batch),
-                     dim3(256), 0, s, a, kw, vw, seg_rows, max_new_sum, static_cast<uint32_t*>(ck),
+                     dim3(256), 0, s, a, kw, vw, seg_rows, max_rows, max_new_sum, static_cast<uint32_t*>(ck),
                      has_v ? static_cast<uint32_t*>(cv) : nullptr, state, static_cast<const uint32_t*>(k_rows),
                      has_v ? static_cast<const uint32_t*>(v_rows) : nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(cache_append_rows_state_kernel, dim3((a.batch + 255) / 256), dim3(256), 0, s, state, a.batch,
-                     seg_rows, a.k, a.max_summaries);
+  hipLaunchKernelGGL(cache_append_rows_state_kernel, dim3((a.batch + 255) / 256), dim3(256), 0, s, a, state,
+                     seg_rows, max_rows);
   return hipGetLastError();
 }
 

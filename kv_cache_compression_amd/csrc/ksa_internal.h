@@ -75,7 +75,7 @@ struct ChunkArgs {
 struct ChunkPtrs {
   const void* ck;  // cache K [batch, Hkv, slots, Dqk]
   const void* cv;  // cache V (nullptr when V is a K prefix)
-  const int32_t* state;
+  int32_t* state;  // read; only the error word may be written (KSA_CACHE_ERR_BAD_SEGMENT)
   const int64_t* seg_rows;
   const void* q;   // [total_rows, Hq, Dqk]
   const void* k;   // [total_rows, Hkv, Dqk]

@@ -28,10 +28,16 @@ __global__ void __launch_bounds__(256) prefill_chunk_generic_kernel(ChunkArgs a,
   const int64_t rl = brl % a.max_rows;
   const int b = static_cast<int>(brl / a.max_rows);
   const int64_t off = p.seg_rows[b];
-  if (rl >= p.seg_rows[b + 1] - off) return;
+  const int64_t R = p.seg_rows[b + 1] - off;
   const int64_t m = p.state[4 * b], r = p.state[4 * b + 1];
   const int64_t max_sum = a.slots - 1 - a.k - static_cast<int64_t>(a.C) * a.k;
-  if (m < 0 || m > max_sum || r < 0 || r > a.k) return;  // state out of range: skipped
+  // state out of range or segment outside 0..max_rows: skipped, and flagged
+  // by one wave of the sequence
+  if (m < 0 || m > max_sum || r < 0 || r > a.k || R < 0 || R > a.max_rows) {
+    if (rl == 0 && h == 0 && lane == 0) p.state[4 * b + 3] |= KSA_CACHE_ERR_BAD_SEGMENT;
+    return;
+  }
+  if (rl >= R) return;
   const int64_t a0 = m * (a.k + 1) + r;
   const int64_t t_seg = a0 - a0 / (a.k + 1);  // first text index of the segment
   const int kvh = h / (a.hq / a.hkv);

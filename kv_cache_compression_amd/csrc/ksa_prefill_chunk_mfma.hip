@@ -67,10 +67,16 @@ __device__ void chunk_summary_wave(const CkArgs& a, int64_t item, const ChunkPtr
   const int kvh = static_cast<int>((item / a.max_sum_seg) % a.hkv);
   const int b = static_cast<int>(item / (static_cast<int64_t>(a.max_sum_seg) * a.hkv));
   const int m = p.state[4 * b], r = p.state[4 * b + 1];
-  if (m < 0 || m > a.slots - a.sum0 || r < 0 || r > a.k) return;  // state out of range: skipped
   const int64_t off = p.seg_rows[b];
+  const int64_t R = p.seg_rows[b + 1] - off;
+  // state out of range or segment outside 0..max_rows: skipped, and flagged
+  // once per sequence
+  if (m < 0 || m > a.slots - a.sum0 || r < 0 || r > a.k || R < 0 || R > a.max_rows) {
+    if (jl == 0 && kvh == 0 && lane == 0) p.state[4 * b + 3] |= KSA_CACHE_ERR_BAD_SEGMENT;
+    return;
+  }
   const int a0 = m * (a.k + 1) + r;
-  const int a1 = a0 + static_cast<int>(p.seg_rows[b + 1] - off);
+  const int a1 = a0 + static_cast<int>(R);
   const int j = m + jl;
   if (j >= a1 / (a.k + 1)) return;
   const int t_seg = a0 - a0 / (a.k + 1);
@@ -164,7 +170,9 @@ __global__ void __launch_bounds__(256, 2) prefill_chunk_d128_kernel(CkArgs a, Ch
   const int r = __builtin_amdgcn_readfirstlane(p.state[4 * b + 1]);
   if (m < 0 || m > a.slots - a.sum0 || r < 0 || r > a.k) return;  // state out of range: skipped
   const int64_t off = p.seg_rows[b];
-  const int R = static_cast<int>(p.seg_rows[b + 1] - off);
+  const int64_t R64 = p.seg_rows[b + 1] - off;
+  if (R64 < 0 || R64 > a.max_rows) return;  // outside the launch's reach: skipped (flagged by the summary waves)
+  const int R = static_cast<int>(R64);
   const int a0 = m * (a.k + 1) + r, a1 = a0 + R;
   const int t_seg = a0 - a0 / (a.k + 1), t_end = a1 - a1 / (a.k + 1);  // segment text [t_seg, t_end)
   const int p0 = (t_seg / PT) * PT + tile * PT;

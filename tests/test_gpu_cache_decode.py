@@ -88,6 +88,9 @@ def test_append_lifecycle_matches_slot_model(k, C, dtype):
 
 @pytest.mark.parametrize("n_text,k,C", [(45, 4, 2), (40, 4, 2), (3, 4, 2), (30, 3, 20), (50, 4, 0)])
 def test_fill_equals_single_appends(n_text, k, C):
+    """The bulk fill against the oracle's slot model of Fig. 4 stepped
+    through the same L rows (every slot, bit for bit; slots the model never
+    writes keep their sentinel), and against the per-token append path."""
     dev = _dev()
     hkv, D = 2, 16
     L = O.augmented_len(n_text, k)
@@ -95,11 +98,25 @@ def test_fill_equals_single_appends(n_text, k, C):
     p = ksa.Params(k, C, hkv, hkv, D, D, torch.float32)
     c1 = ksa.Cache(p, 1, 16, device=dev)
     c2 = ksa.Cache(p, 1, 16, device=dev)
+    c2.k.fill_(-3.0)
+    c2.v.fill_(-3.0)
     _append_all(c1, rk, rv, n_text, k)
     ksa.ksa_cache_fill(c2, rk[None].to(dev).contiguous(), rv[None].to(dev).contiguous(), n_text)
     torch.cuda.synchronize()
+    model = O.CacheModel(k, C, 16)
+    is_s, _ = O.augmented_rows(n_text, k)
+    for a in range(L):
+        (model.append_summary if is_s[a] else model.append_text)(a)
+    assert c2.state[0].tolist() == [model.m, model.r, 0, 0]
+    ck, cv = c2.k[0].cpu(), c2.v[0].cpu()
+    for s, payload in enumerate(model.slots):
+        if payload is None:
+            assert (ck[:, s] == -3.0).all() and (cv[:, s] == -3.0).all(), s
+        else:
+            assert torch.equal(ck[:, s], rk[payload]) and torch.equal(cv[:, s], rv[payload]), (s, payload)
     assert torch.equal(c1.state, c2.state)
-    assert torch.equal(c1.k, c2.k) and torch.equal(c1.v, c2.v)
+    held = [s for s, pl in enumerate(model.slots) if pl is not None]
+    assert torch.equal(c1.k[:, :, held], c2.k[:, :, held]) and torch.equal(c1.v[:, :, held], c2.v[:, :, held])
 
 
 def test_cache_misuse_sets_error_bits():

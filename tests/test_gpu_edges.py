@@ -122,3 +122,65 @@ def test_split_k_paths_flag_a_bad_summary_read(hq, hkv, dqk, dv, mla):
     assert err[0] & ksa.KSA_CACHE_ERR_BAD_SUMMARY_READ
     assert err[1] == 0 and err[2] == 0
     assert torch.isfinite(out[1].float()).all()
+
+
+@pytest.mark.parametrize("dtype,D,hq,hkv", SHAPES)
+def test_segment_contract_violations_are_flagged(dtype, D, hq, hkv):
+    """Row-wise append and chunked prefill with a segment longer than
+    max_rows, a negative one (decreasing offsets) and a state out of range:
+    those sequences are left untouched (no cache slot, no state, no output
+    row written) and get KSA_CACHE_ERR_BAD_SEGMENT; a valid sequence in the
+    same call is processed as usual (cache slots against the oracle's slot
+    model, outputs against the one-shot oracle rows)."""
+    dev = _dev()
+    k, C, B = 8, 2, 4
+    p = ksa.Params(k, C, hq, hkv, D, D, dtype)
+    c = ksa.Cache(p, B, 16, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(9)
+    c.k.normal_(generator=g)
+    c.v.normal_(generator=g)
+    n = 40
+    L = O.augmented_len(n, k)
+    w = ksa_synth.PrefillWorkload("seg", 1, n, k, C, hq, hkv, D, D, dtype, 1e6, 13)
+    qa, ka, va = ksa_synth.prefill_qkv(w, L)
+    # seq 0 valid (10 rows from an empty cache); seq 1: 20 rows > max_rows;
+    # seq 2: offsets go back by 5; seq 3: r = k + 3 is no cache state
+    st0 = torch.tensor([[0, 0, 0, 0], [1, 2, 0, 0], [2, 0, 0, 0], [1, k + 3, 0, 0]], dtype=torch.int32, device=dev)
+    c.state.copy_(st0)
+    seg = torch.tensor([0, 10, 30, 25, 27], dtype=torch.int64, device=dev)
+    max_rows = 12
+    total = 30
+    rows_q = torch.zeros((total, hq, D), dtype=dtype)
+    rows_k = torch.zeros((total, hkv, D), dtype=dtype)
+    rows_v = torch.zeros((total, hkv, D), dtype=dtype)
+    rows_q[:10], rows_k[:10], rows_v[:10] = qa[0, :10], ka[0, :10], va[0, :10]
+    rows_q, rows_k, rows_v = rows_q.to(dev), rows_k.to(dev), rows_v.to(dev)
+    k0, v0 = c.k.clone(), c.v.clone()
+    out = torch.full((total, hq, D), 7.0, dtype=dtype, device=dev)
+    print(f"segment contract: {dtype} D={D}", flush=True)
+    ksa.ksa_prefill_chunk(c, seg, max_rows, rows_q, rows_k, rows_v, out=out)
+    torch.cuda.synchronize()
+    assert ksa.ksa_cache_read_errors(c) == [0] + [ksa.KSA_CACHE_ERR_BAD_SEGMENT] * 3
+    assert torch.equal(c.state[:, :3], st0[:, :3]) and torch.equal(c.k, k0) and torch.equal(c.v, v0)
+    assert (out[10:] == 7.0).all()       # rows of the skipped sequences untouched
+    ref, _ = O.ksa_attention(qa[0].double().numpy(), ka[0].double().numpy(), va[0].double().numpy(),
+                             n, k, C, p.scale, rows=np.arange(10))
+    tol = 1e-4 if dtype == torch.float32 else 2e-2
+    assert np.abs(out[:10].float().cpu().double().numpy() - ref).max() <= tol
+    c.state[:, 3] = 0
+    ksa.ksa_cache_append_rows(c, seg, max_rows, rows_k, rows_v)
+    torch.cuda.synchronize()
+    assert ksa.ksa_cache_read_errors(c) == [0] + [ksa.KSA_CACHE_ERR_BAD_SEGMENT] * 3
+    st = c.state.cpu()
+    assert torch.equal(st[1:, :3], st0[1:, :3].cpu())
+    assert torch.equal(c.k[1:], k0[1:]) and torch.equal(c.v[1:], v0[1:])
+    # seq 0 advanced over its 10 rows exactly as 10 single appends
+    model = O.CacheModel(k, C, 16)
+    is_s, _ = O.augmented_rows(n, k)
+    for a in range(10):
+        (model.append_summary if is_s[a] else model.append_text)(a)
+    assert st[0, :2].tolist() == [model.m, model.r]
+    for s_, payload in enumerate(model.slots):
+        if payload is not None:
+            assert torch.equal(c.k[0, :, s_].cpu(), ka[0, payload]) and torch.equal(c.v[0, :, s_].cpu(), va[0, payload])

@@ -3,7 +3,8 @@ against the oracle's fp64 gradient of Eq. 10 under the same masks.
 
 The GPU backward consumes its own forward's output and normaliser, as a
 training step would.  Tolerances: fp32 |err| <= 1e-4 (1 + |ref|); bf16
-|err| <= 2e-2 (1 + |ref|) element-wise and relative L2 <= 1.5e-2 per tensor
+|err| <= 2e-2 (1 + |ref|) element-wise, mean |err| <= 2e-3 (1 + mean |ref|)
+(fp32: 1e-5) and relative L2 <= 1.5e-2 per tensor
 (bf16 inputs and outputs, fp32 accumulation, P and dS rounded to bf16 before
 their products on the MFMA path)."""
 import numpy as np
@@ -43,8 +44,12 @@ def _compare(name, got, ref, bf16):
     e = np.abs(got - ref)
     tol = 2e-2 if bf16 else 1e-4
     rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
-    print(f"  {name}: max {e.max():.3e} rel-l2 {rel:.3e} |ref|max {np.abs(ref).max():.2f}", flush=True)
+    print(f"  {name}: max {e.max():.3e} mean {e.mean():.3e} rel-l2 {rel:.3e} |ref|max {np.abs(ref).max():.2f} "
+          f"|ref|mean {np.abs(ref).mean():.3e}", flush=True)
     assert np.all(e <= tol * (1 + np.abs(ref))), name
+    # the mean error, on the same relative footing (the output bound's 2e-3
+    # for bf16; fp32 stays 10x under its own element bound)
+    assert e.mean() <= (2e-3 if bf16 else 1e-5) * (1 + np.abs(ref).mean()), name
     # a relative error needs a reference away from zero: rows that see a
     # single key have dS = P (dP - Delta) = 0 exactly, so dq and dk vanish
     if bf16 and np.linalg.norm(ref) > 1e-3:

@@ -28,8 +28,10 @@ def _np(t):
 def _close(name, got, ref):
     e = np.abs(got - ref)
     rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
-    print(f"  {name}: max {e.max():.3e} rel-l2 {rel:.3e}", flush=True)
+    print(f"  {name}: max {e.max():.3e} mean {e.mean():.3e} rel-l2 {rel:.3e} |ref|mean {np.abs(ref).mean():.3e}",
+          flush=True)
     assert np.all(e <= 2e-2 * (1 + np.abs(ref))), name
+    assert e.mean() <= 2e-3 * (1 + np.abs(ref).mean()), name
     assert rel <= 1.5e-2, name
 
 

@@ -14,6 +14,7 @@ import pytest
 from oracle import ksa_oracle as O
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "fig3_sca_k4_c1_n16.txt")
+GOLDEN_SWA = os.path.join(os.path.dirname(__file__), "golden", "fig3_token_swa_k4_w4_n16.txt")
 
 
 def _label_to_row(lbl, k):
@@ -21,9 +22,9 @@ def _label_to_row(lbl, k):
     return O.text_row(idx, k) if kind == "t" else O.summary_row(idx, k)
 
 
-def _read_golden():
+def _read_golden(path=GOLDEN):
     rows = {}
-    with open(GOLDEN) as f:
+    with open(path) as f:
         for line in f:
             line = line.strip()
             if not line or line.startswith("#"):
@@ -48,6 +49,26 @@ def test_fig3_literal_matches_both_encodings():
     np.testing.assert_array_equal(O.visibility_mask_fast(n, k, C), want)
     for a in range(L):
         assert O.visible_set_eq3(n, k, C, a) == set(np.nonzero(want[a])[0])
+
+
+def _golden_mask(path, n, k):
+    gold = _read_golden(path)
+    L = O.augmented_len(n, k)
+    assert len(gold) == L
+    want = np.zeros((L, L), dtype=bool)
+    for q, keys in gold.items():
+        a = _label_to_row(q, k)
+        for key in keys:
+            want[a, _label_to_row(key, k)] = True
+    return want
+
+
+def test_token_window_literal():
+    """The negative control itself is pinned: a hand-written literal of the
+    token-level window of Fig. 3 (left) with W = 4 over four chunks of 4."""
+    want = _golden_mask(GOLDEN_SWA, 16, 4)
+    assert want.sum() == 93
+    np.testing.assert_array_equal(O.token_swa_mask(16, 4, W=4), want)
 
 
 def test_index_map_eq1():
