@@ -264,6 +264,21 @@ KSA_API int32_t ksa_decode_attn(const ksa_params* p, const ksa_cache* c, int32_t
                         const int32_t* kind, void* out, float* lse, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/* ksa_decode_attn for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * kernels and results, with the split partials kept in a scratch array of
+ * the library instead of a caller workspace.  The array (128 MiB) is device
+ * memory of the library's code object: each GPU the library runs on holds
+ * its own copy from the first launch until the process ends; its address is
+ * looked up on the first call on each device.  The call allocates and frees
+ * nothing.  Every call on a GPU shares that GPU's copy, so calls that
+ * overlap on one GPU (different streams, threads) race: serialise them.  A
+ * shape whose partials exceed the array returns
+ * KSA_STATUS_WORKSPACE_TOO_SMALL before anything is launched.  Arguments,
+ * layouts and errors otherwise as ksa_decode_attn. */
+KSA_API int32_t ksa_decode_attn_noalloc(const ksa_params* p, const ksa_cache* c, int32_t batch, const void* q,
+                                const int32_t* kind, void* out, float* lse, void* stream);
+
 /* Synchronous: copies each sequence's error bits into host_error_bits[batch]
  * (host memory) after the work queued on `stream` has finished. */
 KSA_API int32_t ksa_cache_read_errors(const ksa_params* p, const ksa_cache* c, int32_t batch,

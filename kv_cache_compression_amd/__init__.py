@@ -37,7 +37,7 @@ EXPORTS = (
     "ksa_rope_positions", "ksa_prefill_attn", "ksa_prefill_attn_mode", "ksa_prefill_bwd_workspace_bytes",
     "ksa_prefill_attn_bwd", "ksa_cache_slots", "ksa_cache_reset",
     "ksa_cache_append", "ksa_cache_fill", "ksa_cache_append_rows", "ksa_prefill_chunk", "ksa_decode_workspace_bytes", "ksa_decode_attn",
-    "ksa_cache_read_errors",
+    "ksa_decode_attn_noalloc", "ksa_cache_read_errors",
 )
 
 
@@ -100,6 +100,7 @@ _SIGS = {
     "ksa_prefill_chunk": (_i32, [_P, _C, _i32, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
     "ksa_decode_workspace_bytes": (ctypes.c_size_t, [_P, _i32, _i32]),
     "ksa_decode_attn": (_i32, [_P, _C, _i32, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "ksa_decode_attn_noalloc": (_i32, [_P, _C, _i32, _vp, _vp, _vp, _vp, _vp]),
     "ksa_cache_read_errors": (_i32, [_P, _C, _i32, _vp, _vp]),
 }
 
@@ -406,6 +407,23 @@ def ksa_decode_attn(c: Cache, q: torch.Tensor, kind: torch.Tensor, out: Optional
     pc, cc = p.c(), c.c()
     _check(lib().ksa_decode_attn(ctypes.byref(pc), ctypes.byref(cc), c.batch, _ptr(q), _ptr(kind),
                                  _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def ksa_decode_attn_noalloc(c: Cache, q: torch.Tensor, kind: torch.Tensor, out: Optional[torch.Tensor] = None,
+                            lse: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """ksa_decode_attn with the library's own scratch (no workspace)."""
+    p = c.p
+    _need(q, (c.batch, p.num_q_heads, p.head_dim_qk), p.dtype, "q")
+    _need(kind, (c.batch,), torch.int32, "kind")
+    if out is None:
+        out = torch.empty((c.batch, p.num_q_heads, p.head_dim_v), dtype=p.dtype, device=q.device)
+    _need(out, (c.batch, p.num_q_heads, p.head_dim_v), p.dtype, "out")
+    if lse is not None:
+        _need(lse, (c.batch, p.num_q_heads), torch.float32, "lse")
+    pc, cc = p.c(), c.c()
+    _check(lib().ksa_decode_attn_noalloc(ctypes.byref(pc), ctypes.byref(cc), c.batch, _ptr(q), _ptr(kind),
+                                         _ptr(out), _ptr(lse), _stream(stream)))
     return out
 
 

@@ -391,6 +391,30 @@ int32_t ksa_decode_attn(const ksa_params* p, const ksa_cache* c, int32_t batch, 
                     "decode");
 }
 
+int32_t ksa_decode_attn_noalloc(const ksa_params* p, const ksa_cache* c, int32_t batch, const void* q,
+                                const int32_t* kind, void* out, float* lse, void* stream) {
+  if (int32_t st = check_params(p)) return st;
+  if (int32_t st = check_cache(p, c)) return st;
+  if (batch < 0) return fail(KSA_STATUS_INVALID_ARGUMENT, "negative batch");
+  if (batch == 0) return KSA_STATUS_OK;
+  if (!q || !kind || !out) return fail(KSA_STATUS_INVALID_ARGUMENT, "q/kind/out is NULL");
+  const ksa::DecodeArgs a = decode_args(p, batch, c->max_summaries);
+  const size_t need = ksa::decode_workspace_bytes_used(a, p->dtype);
+  if (need > ksa::kDecodeScratchBytes)
+    return fail(KSA_STATUS_WORKSPACE_TOO_SMALL,
+                "this decode needs %zu scratch bytes, above the allocation-free limit of %zu; "
+                "use ksa_decode_attn with a workspace",
+                need, ksa::kDecodeScratchBytes);
+  void* scratch = nullptr;
+  if (need > 0) {
+    if (int32_t st = hip_status(ksa::decode_scratch(&scratch), "decode_noalloc scratch lookup")) return st;
+  }
+  g_msg[0] = 0;
+  return hip_status(ksa::launch_decode(a, p->dtype, c->k, c->v, c->state, q, kind, out, lse, scratch,
+                                       static_cast<hipStream_t>(stream)),
+                    "decode_noalloc");
+}
+
 int32_t ksa_cache_read_errors(const ksa_params* p, const ksa_cache* c, int32_t batch,
                               int32_t* host_error_bits, void* stream) {
   if (int32_t st = check_params(p)) return st;

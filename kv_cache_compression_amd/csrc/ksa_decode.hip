@@ -16,6 +16,8 @@
 //     Q.K^T on 16x16x32 bf16 MFMA with K rows loaded straight into the MFMA
 //     operand layout, P.V on the vector ALU with one 16-byte V load per lane,
 //     then a second kernel merges the per-split (max, sum, output) partials.
+#include <mutex>
+
 #include "ksa_attend_wave.h"
 #include "ksa_internal.h"
 
@@ -378,6 +380,43 @@ size_t decode_workspace_bytes(const DecodeArgs& a) {
   // sized for either split-K path; the generic path needs none
   const size_t gqa = static_cast<size_t>(a.batch) * a.hq * kDecMaxSplits * (a.dv + 2) * sizeof(float);
   return a.v_is_k_prefix ? decode_mla_workspace_bytes(a) : gqa;
+}
+
+size_t decode_workspace_bytes_used(const DecodeArgs& a, int32_t dtype) {
+  if (decode_mla_supported(a, dtype)) return decode_mla_workspace_bytes_used(a);
+  if (!gqa_fast_ok(a, dtype)) return 0;
+  return static_cast<size_t>(a.batch) * a.hq * choose_splits(a) * (a.dv + 2) * sizeof(float);
+}
+
+// ------------------------------------------------------- allocation-free --
+
+// Scratch of the allocation-free decode (split partials and, for the MLA
+// path, the cut): one copy per GPU, set up by the runtime when this code
+// object is loaded and held until the process ends.  On the host `scratch`
+// names a stand-in, not device memory: host code uses only the address
+// decode_scratch() looks up.  Every call on a GPU shares that GPU's copy;
+// each launch writes every record it later reads, so nothing needs clearing,
+// but calls that overlap on one GPU race.
+const size_t kDecodeScratchBytes = size_t(128) << 20;
+static __device__ __align__(256) char scratch[size_t(128) << 20];
+
+hipError_t decode_scratch(void** ptr) {
+  constexpr int kMaxDev = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDev] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 template <int G>

@@ -192,10 +192,19 @@ static constexpr int kMlaCuCap = 1024;
 // 512 bf16 of the unnormalised output.
 constexpr int kMlaRec = 8 + DV * 2;
 
-// Workspace: the records of at most kMlaCuCap + batch work items, then the
-// per-sequence cut.
-__host__ __device__ inline size_t mla_cut_offset(int batch) {
-  return static_cast<size_t>(kMlaCuCap + batch) * HQ * kMlaRec;
+// Workspace: the records of at most max_items = CUs + batch work items,
+// then the per-sequence cut.
+__host__ __device__ inline size_t mla_cut_offset(int max_items) {
+  return static_cast<size_t>(max_items) * HQ * kMlaRec;
+}
+
+// CU count of the current device, capped at kMlaCuCap (the cut's slots).
+static int mla_cu_count() {
+  int dev = 0, ncu = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    ncu = 256;
+  return ncu > 0 ? (ncu < kMlaCuCap ? ncu : kMlaCuCap) : 256;
 }
 
 __global__ void __launch_bounds__(512, 1) decode_mla_split_kernel(
@@ -209,7 +218,7 @@ __global__ void __launch_bounds__(512, 1) decode_mla_split_kernel(
   __shared__ __attribute__((aligned(16))) float xs[8][64][20];
   char* const lds[NBUF] = {lds0, lds1, lds2};
   if (blockIdx.x == 0 && threadIdx.x < 64)
-    mla_write_cut(a, state, kind, reinterpret_cast<int2*>(ws + mla_cut_offset(a.batch)));
+    mla_write_cut(a, state, kind, reinterpret_cast<int2*>(ws + mla_cut_offset(a.max_items)));
   const MlaItem it = mla_item(a, state, kind, blockIdx.x);
   // wave-uniform: keep them in scalar registers
   const int b = __builtin_amdgcn_readfirstlane(it.b);
@@ -408,7 +417,7 @@ __global__ void __launch_bounds__(256) decode_mla_merge_kernel(MlaArgs a, int32_
   const int b = blockIdx.y;
   // both loads in one round trip: the cut is written for every sequence
   const int kb = kind[b];
-  const int2 cut = reinterpret_cast<const int2*>(ws + mla_cut_offset(a.batch))[b];
+  const int2 cut = reinterpret_cast<const int2*>(ws + mla_cut_offset(a.max_items))[b];
   if (kb < 0) return;
   if (head == 0 && threadIdx.x == 0 && !mla_slice(a, state + 4 * b, kb).ok)
     state[4 * b + 3] |= KSA_CACHE_ERR_BAD_SUMMARY_READ;
@@ -460,8 +469,14 @@ bool decode_mla_supported(const DecodeArgs& a, int32_t dtype) {
          a.hkv == 1 && a.slots < (int64_t(1) << 31) / DQK;
 }
 
+// Any device (up to kMlaCuCap CUs).
 size_t decode_mla_workspace_bytes(const DecodeArgs& a) {
-  return mla_cut_offset(a.batch) + static_cast<size_t>(a.batch) * sizeof(int2);
+  return mla_cut_offset(kMlaCuCap + a.batch) + static_cast<size_t>(a.batch) * sizeof(int2);
+}
+
+// What a launch on the current device uses.
+size_t decode_mla_workspace_bytes_used(const DecodeArgs& a) {
+  return mla_cut_offset(mla_cu_count() + a.batch) + static_cast<size_t>(a.batch) * sizeof(int2);
 }
 
 hipError_t launch_decode_mla(const DecodeArgs& d, const void* ck, int32_t* state, const void* q,
@@ -473,11 +488,7 @@ hipError_t launch_decode_mla(const DecodeArgs& d, const void* ck, int32_t* state
   a.max_summaries = d.max_summaries;
   a.slots = d.slots;
   a.sl = d.scale * kLog2e;
-  int dev = 0, ncu = 256;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    ncu = 256;
-  a.n_cu = ncu > 0 ? (ncu < kMlaCuCap ? ncu : kMlaCuCap) : 256;
+  a.n_cu = mla_cu_count();
   a.max_items = a.n_cu + d.batch;
   if (d.batch > 0) {
     hipLaunchKernelGGL(decode_mla_split_kernel, dim3(a.max_items), dim3(512), 0, s, a,

@@ -113,9 +113,16 @@ struct DecodeArgs {
 };
 
 size_t decode_workspace_bytes(const DecodeArgs& a);
+// workspace a launch on the current device uses (<= decode_workspace_bytes)
+size_t decode_workspace_bytes_used(const DecodeArgs& a, int32_t dtype);
+// allocation-free decode: the size of the file-scope scratch array and its
+// device address on the current device (looked up once per device)
+extern const size_t kDecodeScratchBytes;
+hipError_t decode_scratch(void** ptr);
 // absorbed-MLA split-K decode: bf16, Hq = 128, Hkv = 1, Dqk = 576, Dv = 512
 bool decode_mla_supported(const DecodeArgs& a, int32_t dtype);
 size_t decode_mla_workspace_bytes(const DecodeArgs& a);
+size_t decode_mla_workspace_bytes_used(const DecodeArgs& a);
 hipError_t launch_decode_mla(const DecodeArgs& a, const void* ck, int32_t* state, const void* q,
                              const int32_t* kind, void* out, float* lse, void* ws, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int32_t dtype, const void* ck, const void* cv,

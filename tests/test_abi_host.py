@@ -30,7 +30,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(L):
     decl = _declared()
-    assert len(decl) == 18
+    assert len(decl) == 19
     assert sorted(K.EXPORTS) == decl
     for name in decl:
         assert hasattr(L, name), name
@@ -197,6 +197,14 @@ def test_cache_argument_checks(L):
     nov = K.ksa_cache(16, None, 16, 10)
     rc, _ = _status(L, L.ksa_cache_append(ctypes.byref(p), ctypes.byref(nov), 1, fake, fake, fake, None))
     assert rc == 1
+    # the allocation-free decode validates the same way, before any launch
+    rc, msg = _status(L, L.ksa_decode_attn_noalloc(ctypes.byref(p), ctypes.byref(c), 2, None, fake, fake, None,
+                                                   None))
+    assert rc == 1 and "NULL" in msg
+    rc, _ = _status(L, L.ksa_decode_attn_noalloc(ctypes.byref(p), ctypes.byref(nov), 2, fake, fake, fake, None,
+                                                 None))
+    assert rc == 1
+    assert L.ksa_decode_attn_noalloc(ctypes.byref(p), ctypes.byref(c), 0, None, None, None, None, None) == 0
 
 
 def test_status_strings(L):
@@ -210,3 +218,4 @@ def test_python_binding_requires_gpu_tensors(L):
     q = torch.zeros(1, 576, 4, 64)
     with pytest.raises(ValueError):
         K.ksa_prefill_attn(p, q, torch.zeros(1, 576, 2, 64), torch.zeros(1, 576, 2, 64), 512)
+
