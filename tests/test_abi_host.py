@@ -219,3 +219,23 @@ def test_python_binding_requires_gpu_tensors(L):
     with pytest.raises(ValueError):
         K.ksa_prefill_attn(p, q, torch.zeros(1, 576, 2, 64), torch.zeros(1, 576, 2, 64), 512)
 
+
+def test_table1_ratios_from_library_accounting(L):
+    """Per-token cache of the library's own layout (ksa_cache_slots x bytes
+    per slot) as the history grows, against the ratios the report prints in
+    Table 1 for k = 8, h = 128 heads, d = 128, g = 8 KV heads, d_c = 512,
+    d_r = 64: KSA alone 12.5%, KSA + GQA 0.78%, KSA + MLA 0.22% of
+    multi-head attention's 2 h d values per token (Sec. 3, Table 1)."""
+    k, C, n = 8, 64, 8 * 2 ** 22                 # 33.5M tokens: the fixed regions vanish
+    mha = 2 * 128 * 128                          # K and V of 128 heads of 128 per token
+
+    def per_token(hq, hkv, dqk, dv, absorbed):
+        p = K.Params(k, C, hq, hkv, dqk, dv, torch.bfloat16, v_is_k_prefix=absorbed).c()
+        slots = L.ksa_cache_slots(ctypes.byref(p), n // k)
+        assert slots == 1 + k + C * k + n // k
+        width = dqk if absorbed else dqk + dv    # values per slot and kv head
+        return slots * hkv * width / n
+
+    assert per_token(128, 128, 128, 128, False) / mha == pytest.approx(0.125, rel=1e-3)
+    assert round(100 * per_token(128, 8, 128, 128, False) / mha, 2) == 0.78
+    assert round(100 * per_token(128, 1, 576, 512, True) / mha, 2) == 0.22
