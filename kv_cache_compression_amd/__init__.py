@@ -20,7 +20,9 @@ from typing import Optional, Sequence
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libksa.so")
+# KSA_LIB_PATH selects another build of the same library (for instance the
+# host-sanitized one the CPU tests build); the default is the in-tree build
+LIB_PATH = os.environ.get("KSA_LIB_PATH") or os.path.join(_PKG, "libksa.so")
 
 KSA_DTYPE_BF16 = 0
 KSA_DTYPE_FP32 = 1

@@ -71,9 +71,12 @@ __device__ __forceinline__ int32_t trow(const MfmaArgs& a, int32_t t) { return t
 // the group's query heads to the k + 1 rows j(k+1) .. j(k+1)+k.  Lane
 // (hh, c) = (lane / 16, lane % 16) holds dims 8c .. 8c+7 of head hh of a
 // group of four; the key/value rows of a pass are all loaded before any is
-// used, so a pass costs one memory round trip.
-constexpr int SUM_R = 16;  // key rows per pass
-
+// used, so a pass costs one memory round trip.  SUM_R key rows per pass: 9
+// (one pass) when k <= 8, else 16; rows past the chunk are masked but their
+// loads and dot products are still paid, so the pass is sized to the chunk
+// (at k = 8 a 16-row pass spent 7/16 of this path's vector work on masked
+// rows, and the summary rows took 80 of 1441 us of the 32K prefill).
+template <int SUM_R>
 __device__ void summary_rows_wave(const MfmaArgs& a, int64_t item, const bf16_t* __restrict__ q,
                                   const bf16_t* __restrict__ kx, const bf16_t* __restrict__ vx,
                                   bf16_t* __restrict__ out, float* __restrict__ lse) {
@@ -167,7 +170,12 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_d128_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   if (static_cast<int>(blockIdx.x) < a.n_sum_blocks) {
     const int64_t item = static_cast<int64_t>(blockIdx.x) * 4 + wave;
-    if (item < static_cast<int64_t>(a.batch) * a.hkv * a.M) summary_rows_wave(a, item, q, kx, vx, out, lse);
+    if (item < static_cast<int64_t>(a.batch) * a.hkv * a.M) {
+      if (a.k <= 8)
+        summary_rows_wave<9>(a, item, q, kx, vx, out, lse);
+      else
+        summary_rows_wave<16>(a, item, q, kx, vx, out, lse);
+    }
     return;
   }
 
