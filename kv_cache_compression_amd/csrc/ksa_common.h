@@ -62,6 +62,19 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// x combined with the value of the lane 32 away, on the vector ALU:
+// v_permlane32_swap trades lanes 32..63 of one copy of x with lanes 0..31 of
+// another, so every lane holds both halves' values and computes
+// op(x[low lane], x[high lane]) in the same order.
+__device__ __forceinline__ float with_upper_half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float with_upper_half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Augmented row of text token t (Eq. 1): every complete chunk before it adds
 // one summary row.
 __device__ __forceinline__ int64_t text_row(int64_t t, int32_t k) { return t + t / k; }

@@ -351,7 +351,7 @@ __global__ void __launch_bounds__(512, 1) decode_mla_split_kernel(
     float tmax = kNegInf;
 #pragma unroll
     for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[r]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * a.sl;
+    tmax = with_upper_half_max(tmax) * a.sl;
     if (__any(tmax > m_ref + kLazy)) {
       const float m_new = fmaxf(m_ref, tmax);
       const float alpha = m_ref == kNegInf ? 0.f : fast_exp2(m_ref - m_new);
@@ -400,7 +400,7 @@ __global__ void __launch_bounds__(512, 1) decode_mla_split_kernel(
   __builtin_amdgcn_s_waitcnt(0x0070);  // no LDS write in flight at exit
 
   // ---- this range's partial (both waves of a pair hold the same m and l) ----
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = with_upper_half_sum(l_run);
   char* rec = ws + (static_cast<int64_t>(blockIdx.x) * HQ + head) * kMlaRec;
   if (half == 0 && hf == 0) {
     reinterpret_cast<float*>(rec)[0] = m_ref;

@@ -50,6 +50,24 @@ __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 
 // element (v.y) reads element 0 with this compiler.
 __device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2_t, w); }
 
+// Cross-lane reductions on the vector ALU (no LDS round trip):
+//   - sum16: the sum over each group of 16 lanes, in every lane of the
+//     group, by DPP: quad swaps (xor 1, xor 2), then the mirrored half-row
+//     (quad q gets quad 1 - q) and the mirrored row (half h gets half 1 - h);
+//   - with_upper_half_max / with_upper_half_sum (ksa_common.h) for the lane
+//     32 away.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float sum16(float x) {
+  x += dpp_mov<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+  x += dpp_mov<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+  x += dpp_mov<0x141>(x);  // row_half_mirror
+  x += dpp_mov<0x140>(x);  // row_mirror
+  return x;
+}
+
 // floor(t / d) = (umulhi(t, m) + t) >> l for 0 <= t < 2^31.
 inline void fast_div(uint32_t d, uint32_t* m, uint32_t* l) {
   uint32_t s = 0;

@@ -115,10 +115,7 @@ __device__ void chunk_summary_wave(const CkArgs& a, int64_t item, const ChunkPtr
 #pragma unroll
       for (int w = 0; w < 4; ++w)
         part = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qw[w]), as_bf16x2(kw[w]), part, false);
-      part += __shfl_xor(part, 8);
-      part += __shfl_xor(part, 4);
-      part += __shfl_xor(part, 2);
-      part += __shfl_xor(part, 1);
+      part = sum16(part);
       const float sc = part * a.sl;
       const float mx = fmaxf(m_run, sc);
       const float al = m_run == kNegInf ? 0.f : fast_exp2(m_run - mx);
@@ -342,7 +339,19 @@ __global__ void __launch_bounds__(256, 2) prefill_chunk_d128_kernel(CkArgs a, Ch
     for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) t = fmaxf(t, sacc[kb2][rr]);
-    return fmaxf(t, __shfl_xor(t, 32)) * a.sl;
+    return with_upper_half_max(t) * a.sl;
+  };
+
+  // O^T += V^T P^T for 16 keys (k-slot ks of a tile).
+  auto pv_of = [&](const char* vl, const u32x4_t* pw, int ks) __attribute__((always_inline)) {
+    const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, pw[ks]);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const bf16x4_t lo = lds_read_tr(vl, voff[0][db] + 16 * ROW_BYTES * ks);
+      const bf16x4_t hi = lds_read_tr(vl, voff[1][db] + 16 * ROW_BYTES * ks);
+      const bf16x8_t vop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop, oacc[db], 0, 0, 0);
+    }
   };
 
   float m_cur = kNegInf, m_nxt = kNegInf;
@@ -379,20 +388,11 @@ __global__ void __launch_bounds__(256, 2) prefill_chunk_d128_kernel(CkArgs a, Ch
       }
     };
     p_half(0);
-    mask_tile(d1, s_nxt);  // past the last tile S is never used
+    mask_tile(d1, s_nxt);
     const char* vl = lds_v[cur];
     p_half(1);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, pw[ks]);
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const bf16x4_t lo = lds_read_tr(vl, voff[0][db] + 16 * ROW_BYTES * ks);
-        const bf16x4_t hi = lds_read_tr(vl, voff[1][db] + 16 * ROW_BYTES * ks);
-        const bf16x8_t vop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop, oacc[db], 0, 0, 0);
-      }
-    }
+    for (int ks = 0; ks < 4; ++ks) pv_of(vl, pw, ks);
     const float tmax = tile_max(s_nxt);
     grow = __any(tmax > m_cur + kLazyRescale);
     m_nxt = grow ? fmaxf(m_cur, tmax) : m_cur;
@@ -415,13 +415,55 @@ __global__ void __launch_bounds__(256, 2) prefill_chunk_d128_kernel(CkArgs a, Ch
   m_nxt = tile_max(sa);
   grow = true;
   __syncthreads();
-  for (int tt = 0; tt < n_total; tt += 2) {
+  // Every tile but the last goes through the pipeline (which also forms the
+  // next tile's scores); the last tile, always in the segment's own text run,
+  // only needs its P and P V, and its upper 32 keys only when a query of the
+  // wave reaches them.
+  const int n_loop = n_total - 1;
+  for (int tt = 0; tt < n_loop; tt += 2) {
     iter(std::integral_constant<int, 0>(), tt, sa, sb);
-    if (tt + 1 < n_total) iter(std::integral_constant<int, 1>(), tt + 1, sb, sa);
+    if (tt + 1 < n_loop) iter(std::integral_constant<int, 1>(), tt + 1, sb, sa);
+  }
+  {
+    const int tl = n_total - 1;
+    const f32x16_t* s_last = (tl & 1) ? sb : sa;
+    const char* vl = (tl & 1) ? lds_v[1] : lds_v[0];
+    const float alpha = m_cur == kNegInf ? 0.f : fast_exp2(m_cur - m_nxt);
+    if (grow) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) oacc[db][rr] *= alpha;
+    }
+    l_run *= alpha;
+    m_cur = m_nxt;
+    const float nm = m_cur == kNegInf ? 0.f : -m_cur;
+    u32x4_t pw[4];
+    auto p_half = [&](int kb2) __attribute__((always_inline)) {
+#pragma unroll
+      for (int rr = 0; rr < 16; rr += 2) {
+        const float p0f = fast_exp2(fmaf(s_last[kb2][rr], a.sl, nm));
+        const float p1f = fast_exp2(fmaf(s_last[kb2][rr + 1], a.sl, nm));
+        const uint32_t w = pk_bf16(p0f, p1f);
+        pw[2 * kb2 + (rr >> 3)][(rr & 7) >> 1] = w;
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), __builtin_bit_cast(bf16x2_t, one2),
+                                                l_run, false);
+      }
+    };
+    p_half(0);
+    pv_of(vl, pw, 0);
+    pv_of(vl, pw, 1);
+    const TileDesc dl = tile_run(tl);
+    const bool hi_live = dl.run >= 2 ? dl.key0 + 32 <= iw1 : dl.key0 + 32 <= cw1 - a.C - 1;
+    if (hi_live) {
+      p_half(1);
+      pv_of(vl, pw, 2);
+      pv_of(vl, pw, 3);
+    }
   }
   const float m_ref = m_cur;
   if (!wave_active) return;
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = with_upper_half_sum(l_run);
   if (!q_valid) return;
   const float inv = 1.f / l_tot;
   bf16_t* op = static_cast<bf16_t*>(p.out) + (qrow * a.hq + h) * D;

@@ -119,10 +119,7 @@ __device__ void summary_rows_wave(const MfmaArgs& a, int64_t item, const bf16_t*
                                                as_bf16x2(kw[r].z), part, false);
         part = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qw.w),
                                                as_bf16x2(kw[r].w), part, false);
-        part += __shfl_xor(part, 8);
-        part += __shfl_xor(part, 4);
-        part += __shfl_xor(part, 2);
-        part += __shfl_xor(part, 1);
+        part = sum16(part);
         sc[r] = s0 + r < nrows ? part * a.sl : kNegInf;
         mx = fmaxf(mx, sc[r]);
       }
@@ -370,7 +367,31 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_d128_kernel(
     for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
       for (int r = 0; r < 16; ++r) t = fmaxf(t, sacc[kb2][r]);
-    return fmaxf(t, __shfl_xor(t, 32)) * a.sl;
+    return with_upper_half_max(t) * a.sl;
+  };
+
+  // P (bf16) of one 32-key half of a score tile and its row-sum share.
+  auto p_of = [&](const f32x16_t* sc, int kb2, float nm, u32x4_t* pw) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const float p0f = fast_exp2(fmaf(sc[kb2][r], a.sl, nm));
+      const float p1f = fast_exp2(fmaf(sc[kb2][r + 1], a.sl, nm));
+      const uint32_t w = pk_bf16(p0f, p1f);
+      pw[2 * kb2 + (r >> 3)][(r & 7) >> 1] = w;
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w),
+                                              __builtin_bit_cast(bf16x2_t, one2), l_run, false);
+    }
+  };
+  // O^T += V^T P^T for 16 keys (k-slot ks of a tile).
+  auto pv_of = [&](const char* vl, const u32x4_t* pw, int ks) __attribute__((always_inline)) {
+    const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, pw[ks]);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const bf16x4_t lo = lds_read_tr(vl, voff[0][db] + 16 * ROW_BYTES * ks);
+      const bf16x4_t hi = lds_read_tr(vl, voff[1][db] + 16 * ROW_BYTES * ks);
+      const bf16x8_t vop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop, oacc[db], 0, 0, 0);
+    }
   };
 
   // Software pipeline.  Iteration tt: (A) the MFMAs of S for tile tt + 1
@@ -404,17 +425,7 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_d128_kernel(
     const float nm = m_cur == kNegInf ? 0.f : -m_cur;
     u32x4_t pw[4];
     // P of the first 32-key half here, the second half in phase B
-    auto p_half = [&](int kb2) {
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0f = fast_exp2(fmaf(s_cur[kb2][r], a.sl, nm));
-        const float p1f = fast_exp2(fmaf(s_cur[kb2][r + 1], a.sl, nm));
-        const uint32_t w = pk_bf16(p0f, p1f);
-        pw[2 * kb2 + (r >> 3)][(r & 7) >> 1] = w;
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w),
-                                                __builtin_bit_cast(bf16x2_t, one2), l_run, false);
-      }
-    };
+    auto p_half = [&](int kb2) { p_of(s_cur, kb2, nm, pw); };
     p_half(0);
     asm volatile("" : "+v"(pw[0]));
     asm volatile("" : "+v"(pw[1]));
@@ -425,16 +436,7 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_d128_kernel(
     const char* vl = lds_v[cur];
     p_half(1);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, pw[ks]);
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const bf16x4_t lo = lds_read_tr(vl, voff[0][db] + 16 * ROW_BYTES * ks);
-        const bf16x4_t hi = lds_read_tr(vl, voff[1][db] + 16 * ROW_BYTES * ks);
-        const bf16x8_t vop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop, oacc[db], 0, 0, 0);
-      }
-    }
+    for (int ks = 0; ks < 4; ++ks) pv_of(vl, pw, ks);
     const float tmax = tile_max(s_nxt);
     grow = __any(tmax > m_cur + kLazyRescale);
     m_nxt = grow ? fmaxf(m_cur, tmax) : m_cur;
@@ -454,14 +456,45 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_d128_kernel(
     m_nxt = tmax;
     __syncthreads();
   }
-  for (int tt = 0; tt < n_total; tt += 2) {
+  // The loop runs every tile but the last, each iteration also forming the
+  // scores of the next tile; the last tile only needs its P and P V (its
+  // upper 32 keys are skipped when no query of the wave sees them, as on
+  // the diagonal tile that ends every text run).
+  const int n_loop = n_total - 1;
+  for (int tt = 0; tt < n_loop; tt += 2) {
     iter(std::integral_constant<int, 0>(), tt, sa, sb);
-    if (tt + 1 < n_total) iter(std::integral_constant<int, 1>(), tt + 1, sb, sa);
+    if (tt + 1 < n_loop) iter(std::integral_constant<int, 1>(), tt + 1, sb, sa);
+  }
+  if (n_total > 0) {
+    const int tl = n_total - 1;
+    const f32x16_t* s_last = (tl & 1) ? sb : sa;
+    const char* vl = (tl & 1) ? lds_v[1] : lds_v[0];
+    const float alpha = m_cur == kNegInf ? 0.f : fast_exp2(m_cur - m_nxt);
+    if (grow) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
+    l_run *= alpha;
+    m_cur = m_nxt;
+    const float nm = m_cur == kNegInf ? 0.f : -m_cur;
+    u32x4_t pw[4];
+    p_of(s_last, 0, nm, pw);
+    pv_of(vl, pw, 0);
+    pv_of(vl, pw, 1);
+    const int key0 = tl < ns ? tl * BN : t0 + (tl - ns) * BN;
+    const bool hi_live = tl < ns ? key0 + 32 <= cw1 - a.C - 1 : key0 + 32 <= iw1;
+    if (hi_live) {
+      p_of(s_last, 1, nm, pw);
+      pv_of(vl, pw, 2);
+      pv_of(vl, pw, 3);
+    }
   }
   const float m_ref = m_cur;
 
   if (!wave_active) return;
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = with_upper_half_sum(l_run);
   if (!q_valid) return;
   const float inv = 1.f / l_tot;
   const int orow = trow(a, qi);
