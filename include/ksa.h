@@ -141,6 +141,22 @@ KSA_API int32_t ksa_rope_positions(const ksa_params* p, int64_t rows, const int6
 KSA_API int32_t ksa_prefill_attn(const ksa_params* p, int32_t batch, int64_t n_text, const void* q,
                          const void* k, const void* v, void* out, float* lse, void* stream);
 
+/* ksa_prefill_attn with the query's rotary embedding applied as the kernel
+ * loads each query row (Sec. 2.2.1: a text token's position id is its text
+ * index, a summary token's is that of its chunk's last text token).  q holds
+ * the un-rotated queries and is not written; each row is rotated half-split
+ * over all Dqk columns, pair (f, f + Dqk/2) by pos * rope_theta^(-2f/Dqk)
+ * radians, as ksa_rope_augmented(q, rot_off 0, rot_dim Dqk, rope_theta)
+ * would store it (rotation in fp32 or better, rounded to the dtype).  k must
+ * already be rotated: the cache keeps post-RoPE keys (Sec. 2.3.1), so the
+ * keys' pass stays separate.  Same shapes, kernels and errors as
+ * ksa_prefill_attn, plus: rope_theta not positive and finite, or Dqk odd,
+ * is KSA_STATUS_INVALID_ARGUMENT; v_is_k_prefix (whose rotary part is a
+ * column block, not the whole head) is KSA_STATUS_UNSUPPORTED. */
+KSA_API int32_t ksa_prefill_attn_qrope(const ksa_params* p, int32_t batch, int64_t n_text, const void* q,
+                               const void* k, const void* v, void* out, float* lse, double rope_theta,
+                               void* stream);
+
 /* Summary-free baselines the report compares KSA with (Fig. 3; the
  * Hybrid-SCA / Hybrid-SWA comparisons), laid over the same Eq. 1 layout so
  * that the same inputs can be timed against KSA:

@@ -36,10 +36,10 @@ KSA_CACHE_ERR_BAD_SEGMENT = 16
 # Every symbol the header declares.
 EXPORTS = (
     "ksa_status_string", "ksa_last_error_message", "ksa_augmented_len", "ksa_rope_augmented",
-    "ksa_rope_positions", "ksa_prefill_attn", "ksa_prefill_attn_mode", "ksa_prefill_bwd_workspace_bytes",
-    "ksa_prefill_attn_bwd", "ksa_cache_slots", "ksa_cache_reset",
-    "ksa_cache_append", "ksa_cache_fill", "ksa_cache_append_rows", "ksa_prefill_chunk", "ksa_decode_workspace_bytes", "ksa_decode_attn",
-    "ksa_decode_attn_noalloc", "ksa_cache_read_errors",
+    "ksa_rope_positions", "ksa_prefill_attn", "ksa_prefill_attn_qrope", "ksa_prefill_attn_mode",
+    "ksa_prefill_bwd_workspace_bytes", "ksa_prefill_attn_bwd", "ksa_cache_slots", "ksa_cache_reset",
+    "ksa_cache_append", "ksa_cache_fill", "ksa_cache_append_rows", "ksa_prefill_chunk", "ksa_decode_workspace_bytes",
+    "ksa_decode_attn", "ksa_decode_attn_noalloc", "ksa_cache_read_errors",
 )
 
 
@@ -91,6 +91,7 @@ _SIGS = {
     "ksa_rope_augmented": (_i32, [_P, _i32, _i64, _vp, _i32, _i32, _i32, _i32, ctypes.c_double, _vp]),
     "ksa_rope_positions": (_i32, [_P, _i64, _vp, _vp, _i32, _i32, _i32, _i32, ctypes.c_double, _vp]),
     "ksa_prefill_attn": (_i32, [_P, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "ksa_prefill_attn_qrope": (_i32, [_P, _i32, _i64, _vp, _vp, _vp, _vp, _vp, ctypes.c_double, _vp]),
     "ksa_prefill_attn_mode": (_i32, [_P, _i32, _i64, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
     "ksa_prefill_bwd_workspace_bytes": (ctypes.c_size_t, [_P, _i32, _i64]),
     "ksa_prefill_attn_bwd": (_i32, [_P, _i32, _i64, _i32, _i64] + [_vp] * 10 + [ctypes.c_size_t, _vp]),
@@ -236,6 +237,20 @@ def ksa_prefill_attn(p: Params, q: torch.Tensor, k: torch.Tensor, v: Optional[to
     _check(lib().ksa_prefill_attn(ctypes.byref(pc), B, n_text, _ptr(q), _ptr(k),
                                   None if p.v_is_k_prefix else _ptr(v), _ptr(out), _ptr(lse),
                                   _stream(stream)))
+    return out
+
+
+def ksa_prefill_attn_qrope(p: Params, q: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tensor], n_text: int,
+                           rope_theta: float, out: Optional[torch.Tensor] = None,
+                           lse: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """:func:`ksa_prefill_attn` on un-rotated queries: each query row is
+    rotated (half-split over all Dqk columns, report Sec. 2.2.1 positions) as
+    the kernel loads it; ``q`` is not written, ``k`` must be rotated already."""
+    B, out = _prefill_buffers(p, q, k, v, n_text, out, lse)
+    pc = p.c()
+    _check(lib().ksa_prefill_attn_qrope(ctypes.byref(pc), B, n_text, _ptr(q), _ptr(k),
+                                        None if p.v_is_k_prefix else _ptr(v), _ptr(out), _ptr(lse),
+                                        float(rope_theta), _stream(stream)))
     return out
 
 

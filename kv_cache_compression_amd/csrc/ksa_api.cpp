@@ -1,6 +1,7 @@
 // C ABI of the KSA library: argument checks, dispatch to the kernels.
 // Every entry point validates on the host before launching anything and
 // returns a ksa_status; details go to a thread-local message.
+#include <cmath>
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -190,14 +191,17 @@ ksa::PrefillArgs prefill_args(const ksa_params* p, int32_t mode, int64_t window_
   a.mode = mode;
   // a window wider than the sequence is the whole causal prefix
   a.window_tokens = mode == KSA_MODE_SWA ? (window_tokens < n_text ? window_tokens : n_text) : 0;
+  a.rope_theta = 0.0;
   return a;
 }
 
 }  // namespace
 
-int32_t ksa_prefill_attn_mode(const ksa_params* p, int32_t mode, int64_t window_tokens, int32_t batch,
-                              int64_t n_text, const void* q, const void* k, const void* v, void* out,
-                              float* lse, void* stream) {
+namespace {
+
+int32_t prefill_launch(const ksa_params* p, int32_t mode, int64_t window_tokens, int32_t batch, int64_t n_text,
+                       const void* q, const void* k, const void* v, void* out, float* lse, double rope_theta,
+                       void* stream) {
   if (int32_t st = check_params(p)) return st;
   if (int32_t st = check_mode(mode, window_tokens)) return st;
   if (batch < 0 || n_text < 0) return fail(KSA_STATUS_INVALID_ARGUMENT, "negative batch/n_text");
@@ -205,7 +209,8 @@ int32_t ksa_prefill_attn_mode(const ksa_params* p, int32_t mode, int64_t window_
   if (batch == 0 || n_text == 0) return KSA_STATUS_OK;
   if (!q || !k || !out || (!p->v_is_k_prefix && !v))
     return fail(KSA_STATUS_INVALID_ARGUMENT, "q/k/v/out pointer is NULL");
-  const ksa::PrefillArgs a = prefill_args(p, mode, window_tokens, batch, n_text);
+  ksa::PrefillArgs a = prefill_args(p, mode, window_tokens, batch, n_text);
+  a.rope_theta = rope_theta;
   g_msg[0] = 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (ksa::prefill_mfma_supported(a, p->dtype))
@@ -213,6 +218,25 @@ int32_t ksa_prefill_attn_mode(const ksa_params* p, int32_t mode, int64_t window_
   if (ksa::prefill_mla_supported(a, p->dtype))
     return hip_status(ksa::launch_prefill_mla(a, k, q, out, lse, s), "prefill");
   return hip_status(ksa::launch_prefill_generic(a, p->dtype, 0, q, k, v, out, lse, s), "prefill");
+}
+
+}  // namespace
+
+int32_t ksa_prefill_attn_mode(const ksa_params* p, int32_t mode, int64_t window_tokens, int32_t batch,
+                              int64_t n_text, const void* q, const void* k, const void* v, void* out,
+                              float* lse, void* stream) {
+  return prefill_launch(p, mode, window_tokens, batch, n_text, q, k, v, out, lse, 0.0, stream);
+}
+
+int32_t ksa_prefill_attn_qrope(const ksa_params* p, int32_t batch, int64_t n_text, const void* q, const void* k,
+                               const void* v, void* out, float* lse, double rope_theta, void* stream) {
+  if (int32_t st = check_params(p)) return st;
+  if (!(rope_theta > 0.0) || !std::isfinite(rope_theta))
+    return fail(KSA_STATUS_INVALID_ARGUMENT, "rope_theta must be positive and finite");
+  if (p->head_dim_qk % 2) return fail(KSA_STATUS_INVALID_ARGUMENT, "head_dim_qk must be even for RoPE");
+  if (p->v_is_k_prefix)
+    return fail(KSA_STATUS_UNSUPPORTED, "fused query RoPE of the absorbed (v_is_k_prefix) form");
+  return prefill_launch(p, KSA_MODE_KSA, 0, batch, n_text, q, k, v, out, lse, rope_theta, stream);
 }
 
 // [delta: batch * Hq * L fp32, 256-byte aligned][MFMA path: summary-key partials]

@@ -74,6 +74,16 @@ __device__ __forceinline__ float with_upper_half_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+// The same for the lane 16 away within each half wave: v_permlane16_swap
+// trades the odd 16-lane rows of one copy with the even rows of another.
+__device__ __forceinline__ float with_row_pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float with_row_pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // Augmented row of text token t (Eq. 1): every complete chunk before it adds
 // one summary row.
@@ -81,6 +91,19 @@ __device__ __forceinline__ int64_t text_row(int64_t t, int32_t k) { return t + t
 // Augmented row of summary s_j: last row of chunk j.
 __device__ __forceinline__ int64_t summary_row(int64_t j, int32_t k) {
   return j * (k + 1) + k;
+}
+
+// Position id of augmented row a for n text tokens and chunk size k
+// (Sec. 2.2.1: text keeps its text index, a summary takes the id of its
+// chunk's last text token).
+__device__ __forceinline__ int64_t augmented_position(int64_t a, int64_t n, int32_t k) {
+  const int64_t M = n / k;
+  if (a < M * (k + 1)) {
+    const int64_t c = a / (k + 1);
+    const int64_t o = a - c * (k + 1);
+    return c * k + (o < k ? o : k - 1);  // summary: the chunk's last text position
+  }
+  return M * k + (a - M * (k + 1));  // trailing partial chunk
 }
 
 }  // namespace ksa

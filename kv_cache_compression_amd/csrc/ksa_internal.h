@@ -29,6 +29,8 @@ struct PrefillArgs {
   float scale;
   int32_t mode;           // KSA_MODE_*
   int64_t window_tokens;  // W of KSA_MODE_SWA
+  double rope_theta;      // > 0: q is un-rotated; each row is rotated (half-split over all Dqk
+                          // columns, Sec. 2.2.1 positions) as it is loaded.  0: q is rotated.
 };
 
 // Generic prefill over a subset of augmented rows: rows_kind selects

@@ -124,11 +124,8 @@ __device__ void summary_dq_wave(const BwdArgs& a, int64_t item, const bf16_t* __
           s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qw[e]), as_bf16x2(kw[r][e]), s, false);
           dp = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(gw[e]), as_bf16x2(vw[r][e]), dp, false);
         }
-#pragma unroll
-        for (int o = 8; o >= 1; o >>= 1) {
-          s += __shfl_xor(s, o);
-          dp += __shfl_xor(dp, o);
-        }
+        s = sum16(s);
+        dp = sum16(dp);
         const float p = fast_exp2(fmaf(s, a.sl, -lse2));
         const float ds = s0 + r < nrows ? p * (dp - dl) : 0.f;
 #pragma unroll
@@ -728,11 +725,12 @@ __global__ void __launch_bounds__(256) bwd_sum_keys_kernel(BwdArgs a, const bf16
     const uint2 xa = is_v ? gw : qw, xb = is_v ? vw : kw;
     float part_dot = bf_lo(xa.x) * bf_lo(xb.x) + bf_hi(xa.x) * bf_hi(xb.x) + bf_lo(xa.y) * bf_lo(xb.y) +
                      bf_hi(xa.y) * bf_hi(xb.y);
-#pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) part_dot += __shfl_xor(part_dot, o);
-    const float other = __shfl_xor(part_dot, 32);
-    const float s = is_v ? other : part_dot;
-    const float dpv = is_v ? part_dot : other;
+    part_dot = with_row_pair_sum(sum16(part_dot));
+    // v_permlane32_swap of a value with itself yields the lower half's copy
+    // in the first result and the upper half's in the second, in every lane
+    const auto both = __builtin_amdgcn_permlane32_swap(__float_as_uint(part_dot), __float_as_uint(part_dot), false, false);
+    const float s = __uint_as_float(both[0]);
+    const float dpv = __uint_as_float(both[1]);
     const int64_t so = (static_cast<int64_t>(b) * a.hq + h) * a.L + srow;
     const float p = fast_exp2(s * a.sl - lse[so] * kLog2e);
     const float ds = p * (dpv - delta[so]);

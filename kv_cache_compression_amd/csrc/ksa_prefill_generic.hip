@@ -48,6 +48,28 @@ __global__ void __launch_bounds__(256) prefill_generic_kernel(PrefillArgs a, int
   WaveAttnState<NQ, NV> st;
   const T* qrow = q + ((static_cast<int64_t>(b) * a.L + row) * a.hq + h) * a.dqk;
   wave_attn_init<T, NQ, NV>(st, qrow, a.dqk, a.scale * kLog2e, lane);
+  if (a.rope_theta > 0.0) {
+    // Sec. 2.2.1 rotary embedding of the query, half-split over all Dqk
+    // columns: pair (f, f + Dqk/2) turns by pos * theta^(-2f/Dqk), in fp64,
+    // rounded to T as a separate rotation pass would store it.
+    const int half = a.dqk / 2;
+    const double pos = static_cast<double>(augmented_position(row, a.n_text, a.k));
+#pragma unroll
+    for (int e = 0; e < NQ; ++e) {
+      const int d = lane + 64 * e;
+      if (d < a.dqk) {
+        const int f = d < half ? d : d - half;
+        double sn, cs;
+        sincos(pos * pow(a.rope_theta, -2.0 * f / a.dqk), &sn, &cs);
+        const double x = load_f32(qrow + d);
+        const double y = load_f32(qrow + (d < half ? d + half : d - half));
+        const double r = d < half ? x * cs - y * sn : x * cs + y * sn;
+        T rt;
+        store_f32(&rt, static_cast<float>(r));
+        st.q[e] = load_f32(&rt) * (a.scale * kLog2e);
+      }
+    }
+  }
 
   // Decode the row through the Eq. 1 layout.
   const int64_t c = row / (a.k + 1);

@@ -38,6 +38,7 @@
 //   - workgroups run longest-first (later queries see more summaries) and,
 //     when the head count allows, all workgroups of one (sequence, kv head)
 //     sit on one XCD so that its K/V stay in that XCD's L2.
+#include <cmath>
 #include <type_traits>
 
 #include "ksa_internal.h"
@@ -60,7 +61,32 @@ struct MfmaArgs {
   float sl;                 // softmax scale * log2(e)
   int32_t mode;             // KSA_MODE_*: summaries and text window of text queries
   int32_t W;                // token window of KSA_MODE_SWA
+  // Query rotary embedding applied on load (the QROT kernels): frequency f
+  // turns by theta^(-2f/128) radians per position; rope_fr[i] is that rate
+  // in revolutions for f = 8 i, rope_ratio steps f by one.
+  double rope_fr[8];
+  double rope_ratio;
 };
+
+// sin and cos of the angle pos * fr revolutions: the product is reduced to
+// [-1/2, 1/2] revolutions in fp64 (exact up to fp64 rounding for any
+// position an int32 holds), then v_sin_f32 / v_cos_f32, which take their
+// argument in revolutions.
+__device__ __forceinline__ void rope_sincos(double pos, double fr, float* sn, float* cs) {
+  const double x = pos * fr;
+  const float r = static_cast<float>(x - rint(x));
+  *sn = __builtin_amdgcn_sinf(r);
+  *cs = __builtin_amdgcn_cosf(r);
+}
+
+// Sec. 2.2.1 half-split rotation of one (x, partner) pair of bf16x2 words:
+// lower-half dims get x cos - y sin, upper-half dims x cos + y sin, in fp32,
+// rounded to bf16 as a separate rotation pass would store them.
+__device__ __forceinline__ uint32_t rope_pair(uint32_t x, uint32_t y, bool upper, float sn0, float cs0, float sn1,
+                                              float cs1) {
+  const float s0 = upper ? sn0 : -sn0, s1 = upper ? sn1 : -sn1;
+  return pk_bf16(bf_lo(x) * cs0 + bf_lo(y) * s0, bf_hi(x) * cs1 + bf_hi(y) * s1);
+}
 
 __device__ __forceinline__ int32_t div_k(const MfmaArgs& a, int32_t t) {
   return fast_div_apply(t, a.divk_m, a.divk_l);
@@ -76,7 +102,7 @@ __device__ __forceinline__ int32_t trow(const MfmaArgs& a, int32_t t) { return t
 // loads and dot products are still paid, so the pass is sized to the chunk
 // (at k = 8 a 16-row pass spent 7/16 of this path's vector work on masked
 // rows, and the summary rows took 80 of 1441 us of the 32K prefill).
-template <int SUM_R>
+template <int SUM_R, bool QROT>
 __device__ void summary_rows_wave(const MfmaArgs& a, int64_t item, const bf16_t* __restrict__ q,
                                   const bf16_t* __restrict__ kx, const bf16_t* __restrict__ vx,
                                   bf16_t* __restrict__ out, float* __restrict__ lse) {
@@ -96,8 +122,27 @@ __device__ void summary_rows_wave(const MfmaArgs& a, int64_t item, const bf16_t*
     const int hloc = hg + hh;
     const bool hval = hloc < a.g;
     const int h = kvh * a.g + (hval ? hloc : 0);
-    const u32x4_t qw = *reinterpret_cast<const u32x4_t*>(
+    u32x4_t qw = *reinterpret_cast<const u32x4_t*>(
         q + (static_cast<int64_t>(b) * a.L + srow_a) * a.hq * D + static_cast<int64_t>(h) * D + 8 * c);
+    if constexpr (QROT) {
+      // position of s_j: its chunk's last text token; dims 8c .. 8c+7 pair
+      // with dims 8c +- 64, which lane c ^ 8 of the same 16 holds
+      const double pos = static_cast<double>(j + 1) * a.k - 1;
+      double fr = a.rope_fr[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) fr = (c & 7) == i ? a.rope_fr[i] : fr;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t y = static_cast<uint32_t>(
+            __builtin_amdgcn_update_dpp(0, static_cast<int>(qw[w]), 0x128, 0xF, 0xF, false));  // row_ror:8
+        float sn0, cs0, sn1, cs1;
+        rope_sincos(pos, fr, &sn0, &cs0);
+        fr *= a.rope_ratio;
+        rope_sincos(pos, fr, &sn1, &cs1);
+        fr *= a.rope_ratio;
+        qw[w] = rope_pair(qw[w], y, c >= 8, sn0, cs0, sn1, cs1);
+      }
+    }
     float m = kNegInf, l = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < nrows; s0 += SUM_R) {
       u32x4_t kw[SUM_R], vw[SUM_R];
@@ -156,7 +201,7 @@ __device__ void summary_rows_wave(const MfmaArgs& a, int64_t item, const bf16_t*
 
 }  // namespace
 
-template <int HPW>
+template <int HPW, bool QROT>
 __global__ void __launch_bounds__(256, 2) prefill_mfma_d128_kernel(
     MfmaArgs a, const bf16_t* __restrict__ q, const bf16_t* __restrict__ kx,
     const bf16_t* __restrict__ vx, bf16_t* __restrict__ out, float* __restrict__ lse) {
@@ -169,9 +214,9 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_d128_kernel(
     const int64_t item = static_cast<int64_t>(blockIdx.x) * 4 + wave;
     if (item < static_cast<int64_t>(a.batch) * a.hkv * a.M) {
       if (a.k <= 8)
-        summary_rows_wave<9>(a, item, q, kx, vx, out, lse);
+        summary_rows_wave<9, QROT>(a, item, q, kx, vx, out, lse);
       else
-        summary_rows_wave<16>(a, item, q, kx, vx, out, lse);
+        summary_rows_wave<16, QROT>(a, item, q, kx, vx, out, lse);
     }
     return;
   }
@@ -232,6 +277,29 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_d128_kernel(
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
       qop[ks] = q_valid ? *reinterpret_cast<const bf16x8_t*>(qp + 16 * ks) : bf16x8_t{};
+    if constexpr (QROT) {
+      // text t_qi sits at position qi; dims f = 16 ks + 8 half + j (ks < 4)
+      // and f + 64 are both in this lane
+      const double pos = static_cast<double>(qi);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        u32x4_t lo = __builtin_bit_cast(u32x4_t, qop[ks]), hi = __builtin_bit_cast(u32x4_t, qop[ks + 4]);
+        double fr = half ? a.rope_fr[2 * ks + 1] : a.rope_fr[2 * ks];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          float sn0, cs0, sn1, cs1;
+          rope_sincos(pos, fr, &sn0, &cs0);
+          fr *= a.rope_ratio;
+          rope_sincos(pos, fr, &sn1, &cs1);
+          fr *= a.rope_ratio;
+          const uint32_t x = lo[w], y = hi[w];
+          lo[w] = rope_pair(x, y, false, sn0, cs0, sn1, cs1);
+          hi[w] = rope_pair(y, x, true, sn0, cs0, sn1, cs1);
+        }
+        qop[ks] = __builtin_bit_cast(bf16x8_t, lo);
+        qop[ks + 4] = __builtin_bit_cast(bf16x8_t, hi);
+      }
+    }
   }
 
   // Tile loads: thread owns 16-byte chunk (tid % 16) of rows tid/16 + 16 u
@@ -548,11 +616,24 @@ static hipError_t launch_hpw(const PrefillArgs& p, const void* q, const void* k,
   a.W = static_cast<int32_t>(p.window_tokens);
   const int64_t sum_items = static_cast<int64_t>(a.batch) * a.hkv * a.M;
   a.n_sum_blocks = static_cast<int32_t>(((sum_items + 3) / 4 + 7) / 8 * 8);  // keeps text blocks XCD-aligned
+  for (int i = 0; i < 8; ++i) a.rope_fr[i] = 0.0;
+  a.rope_ratio = 0.0;
+  const bool qrot = p.rope_theta > 0.0;
+  if (qrot) {
+    constexpr double kTwoPi = 6.283185307179586;
+    for (int i = 0; i < 8; ++i) a.rope_fr[i] = std::pow(p.rope_theta, -16.0 * i / D) / kTwoPi;
+    a.rope_ratio = std::pow(p.rope_theta, -2.0 / D);
+  }
   const int64_t blocks = a.n_text_blocks + a.n_sum_blocks;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(prefill_mfma_d128_kernel<HPW>, dim3(static_cast<uint32_t>(blocks)), dim3(256),
-                     0, s, a, static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
-                     static_cast<const bf16_t*>(v), static_cast<bf16_t*>(out), lse);
+  if (qrot)
+    hipLaunchKernelGGL((prefill_mfma_d128_kernel<HPW, true>), dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, s,
+                       a, static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
+                       static_cast<const bf16_t*>(v), static_cast<bf16_t*>(out), lse);
+  else
+    hipLaunchKernelGGL((prefill_mfma_d128_kernel<HPW, false>), dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
+                       s, a, static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
+                       static_cast<const bf16_t*>(v), static_cast<bf16_t*>(out), lse);
   return hipGetLastError();
 }
 

@@ -38,9 +38,16 @@ constexpr int DQK = 576, DV = 512;
 constexpr int HQ = 128;
 constexpr int TK = 32;                  // keys per tile
 constexpr int GRB = DQK * 2;            // bytes per augmented row in HBM: 1152
-constexpr int RB = GRB + 16;            // padded LDS row: 1168 bytes (73 chunks)
-constexpr int RCH = RB / 16;            // 73
-constexpr int TILE_LDS = 37 * 64 * 16;  // 37888 bytes >= 32 x 1168
+// LDS rows are padded to 1184 bytes (74 chunks of 16): 296 dwords, 40 mod
+// the 64 banks, so the 8 rows a half wave reads in a transposing V^T read
+// (8 dwords each) fall on 8 disjoint groups of 8 banks; rows 8 .. 15 of
+// every 16 store their 16-byte chunks pairwise swapped (chunk c at c ^ 1),
+// so the 16 rows of a K operand read (4 dwords each) cover all 64 banks too.
+// (With 1168-byte rows, 36 mod 64, both reads met two-way conflicts.)
+constexpr int RB = GRB + 32;            // 1184
+constexpr int RCH = RB / 16;            // 74
+constexpr int TILE_LDS = 37 * 64 * 16;  // 37888 bytes = 32 x 1184
+static_assert(TILE_LDS == 32 * RB, "a tile fills its buffer exactly");
 constexpr int NBUF = 3;
 constexpr float kLazy = 8.f;
 
@@ -113,12 +120,17 @@ __global__ void __launch_bounds__(512, 1) prefill_mla_kernel(MlaPrefillArgs a, c
     for (int kd = 0; kd < 18; ++kd) qop[kd] = *reinterpret_cast<const bf16x8_t*>(qp + 32 * kd);
   }
 
-  // Tile loads: chunk s = 64 (8 i + wave) + lane of a tile (i < 5,
-  // 8 i + wave < 37) is tile row s / 73, 16-byte chunk s % 73 (chunk 72 is
-  // LDS padding and reads 16 bytes past the row).
+  // Tile loads: LDS chunk s = 64 (8 i + wave) + lane of a tile (i < 5,
+  // 8 i + wave < 37) is tile row s / 74, stored chunk s % 74, which holds
+  // the row's chunk (s % 74) ^ ((row / 8) % 2); chunks 72 and 73 are LDS
+  // padding and read 32 bytes past the row.
   const int nld = wave < 5 ? 5 : 4;
   auto trw = [&](int i) { return ((8 * i + wave) * 64 + lane) / RCH; };
-  auto tch = [&](int i) { return 16 * (((8 * i + wave) * 64 + lane) % RCH); };
+  auto tch = [&](int i) {
+    const int s_ = (8 * i + wave) * 64 + lane;
+    const int r_ = s_ / RCH;
+    return 16 * ((s_ - r_ * RCH) ^ ((r_ >> 3) & 1));
+  };
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<bf16_t*>(kx + static_cast<int64_t>(b) * a.L * DQK), static_cast<short>(0), a.L * GRB, 0x00020000);
   auto prefetch = [&](int t, char* buf) __attribute__((always_inline)) {
@@ -160,14 +172,15 @@ __global__ void __launch_bounds__(512, 1) prefill_mla_kernel(MlaPrefillArgs a, c
   if (tid == 0) restart = 0;
   const uint32_t one2 = 0x3f803f80u;
   // K operand (A of 16x16x32): key row lane % 16 (+16), d = 32 kd + 8 (lane / 16) + j
-  const int krow_off = l16 * RB + 16 * g4;
+  // (chunk 4 kd + g4, stored at 4 kd + (g4 ^ 1) in rows 8 .. 15 of 16)
+  const int krow_off = l16 * RB + 16 * (g4 ^ ((l16 >> 3) & 1));
   // V^T operand (A): in 16-lane group g4, lane (4 rr + c4) points at key row
   // 4 g4 + rr (+16 for the upper k-slots) and d = 16 db + 4 c4; the
   // transposing read gives lane i V[4 keys][d = 16 db + i % 16].  The k-slot
   // order {4 g4 .. 4 g4 + 3, 16 + 4 g4 .. 16 + 4 g4 + 3} is the order in which
   // the lane holds its probabilities, so P needs no exchange.
   const int rr = l16 >> 2, c4 = l16 & 3;
-  const int vrow_off = (4 * g4 + rr) * RB + 8 * c4;
+  const int vrow_off = (4 * g4 + rr) * RB + 16 * ((c4 >> 1) ^ ((g4 >> 1) & 1)) + 8 * (c4 & 1);
 
   auto tile_step = [&](auto cur_c, int t, bool first_pass) __attribute__((always_inline)) {
     constexpr int cur = decltype(cur_c)::value;
@@ -202,8 +215,7 @@ __global__ void __launch_bounds__(512, 1) prefill_mla_kernel(MlaPrefillArgs a, c
     float tmax = kNegInf;
 #pragma unroll
     for (int e = 0; e < 8; ++e) tmax = fmaxf(tmax, sv[e]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * a.sl;
+    tmax = with_upper_half_max(with_row_pair_max(tmax)) * a.sl;
     if (first_pass) {
       if (t == 0) m_ref = tmax;
       m_all = fmaxf(m_all, tmax);
@@ -254,8 +266,7 @@ __global__ void __launch_bounds__(512, 1) prefill_mla_kernel(MlaPrefillArgs a, c
     if (!restart) break;
   }
 
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
+  const float l_tot = with_upper_half_sum(with_row_pair_sum(l_run));
   const float inv = 1.f / l_tot;
   bf16_t* op = out + qo * DV + 4 * g4;
 #pragma unroll
@@ -271,7 +282,7 @@ __global__ void __launch_bounds__(512, 1) prefill_mla_kernel(MlaPrefillArgs a, c
 
 bool prefill_mla_supported(const PrefillArgs& a, int32_t dtype) {
   return dtype == KSA_DTYPE_BF16 && a.v_is_k_prefix && a.dqk == DQK && a.dv == DV && a.hq == HQ && a.hkv == 1 &&
-         a.mode == KSA_MODE_KSA && a.L * static_cast<int64_t>(GRB) < (int64_t(1) << 31) &&
+         a.mode == KSA_MODE_KSA && a.L * static_cast<int64_t>(GRB) + RB < (int64_t(1) << 31) &&
          static_cast<int64_t>(a.batch) * a.L < (int64_t(1) << 31);
 }
 

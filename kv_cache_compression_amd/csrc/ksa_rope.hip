@@ -13,17 +13,6 @@
 
 namespace ksa {
 
-// Position id of augmented row a for n text tokens and chunk size k.
-__device__ __forceinline__ int64_t augmented_position(int64_t a, int64_t n, int32_t k) {
-  const int64_t M = n / k;
-  if (a < M * (k + 1)) {
-    const int64_t c = a / (k + 1);
-    const int64_t o = a - c * (k + 1);
-    return c * k + (o < k ? o : k - 1);  // summary: the chunk's last text position
-  }
-  return M * k + (a - M * (k + 1));  // trailing partial chunk
-}
-
 template <typename T>
 __global__ void __launch_bounds__(256) rope_kernel(RopeArgs a, T* __restrict__ x) {
   const int32_t half = a.rot_dim / 2;

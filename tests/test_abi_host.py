@@ -30,7 +30,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(L):
     decl = _declared()
-    assert len(decl) == 19
+    assert len(decl) == 20
     assert sorted(K.EXPORTS) == decl
     for name in decl:
         assert hasattr(L, name), name
@@ -118,6 +118,24 @@ def test_prefill_mode_arguments(L):
     assert rc == 1  # v missing
     for mode in (0, 1, 2):
         assert L.ksa_prefill_attn_mode(ctypes.byref(p), mode, 5, 0, 512, None, None, None, None, None, None) == 0
+
+
+def test_prefill_qrope_arguments(L):
+    p = _params()
+    fake = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    for theta in (0.0, -1.0, float("inf"), float("nan")):
+        rc, msg = _status(L, L.ksa_prefill_attn_qrope(ctypes.byref(p), 1, 512, fake, fake, fake, fake, None, theta,
+                                                      None))
+        assert rc == 1 and "rope_theta" in msg
+    odd = _params(head_dim_qk=63, head_dim_v=64)
+    rc, msg = _status(L, L.ksa_prefill_attn_qrope(ctypes.byref(odd), 1, 512, fake, fake, fake, fake, None, 1e4, None))
+    assert rc == 1 and "even" in msg
+    mla = _params(num_q_heads=128, num_kv_heads=1, head_dim_qk=576, head_dim_v=512, v_is_k_prefix=1)
+    rc, msg = _status(L, L.ksa_prefill_attn_qrope(ctypes.byref(mla), 1, 512, fake, fake, None, fake, None, 1e4, None))
+    assert rc == 2 and "absorbed" in msg
+    rc, _ = _status(L, L.ksa_prefill_attn_qrope(ctypes.byref(p), 1, 512, fake, fake, None, fake, None, 1e4, None))
+    assert rc == 1  # v missing
+    assert L.ksa_prefill_attn_qrope(ctypes.byref(p), 0, 512, None, None, None, None, None, 1e4, None) == 0
 
 
 def test_prefill_bwd_arguments(L):
