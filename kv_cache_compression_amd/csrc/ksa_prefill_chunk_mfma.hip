@@ -19,8 +19,11 @@
 // loads stay direct-to-LDS; a run's last tile masks keys past the run's
 // end.  The compute pipeline is the one-shot kernel's: S^T = K Q^T and
 // O^T += V^T P^T on v_mfma_f32_32x32x16_bf16, lazy rescale, one barrier
-// per tile.  Summary query rows of the segments run in a second, LDS-free
-// launch, one wave per (sequence, kv head, summary).
+// per tile; workgroups run longest-first and, when the slot count allows,
+// all tiles of one (sequence, kv head) sit on one XCD so that the cache's
+// summaries stay in that XCD's L2.  Summary query rows of the segments, one
+// wave per (sequence, kv head, summary), take the last workgroups of the
+// same launch: the shortest work fills the tail.
 #include <type_traits>
 
 #include "ksa_internal.h"
@@ -42,7 +45,7 @@ struct CkArgs {
   uint32_t divk_m, divk_l;
   float sl;
   int32_t slots, sum0;  // cache slots per (sequence, kv head); first summary slot
-  int32_t max_rows, max_sum_seg, n_sum_blocks;
+  int32_t max_rows, max_sum_seg, n_sum_blocks, n_text_blocks, xcd_map;
   int64_t total_rows;
 };
 
@@ -58,7 +61,11 @@ __device__ __forceinline__ int32_t text_slot(const CkArgs& a, int32_t x, int32_t
 }
 
 // Summary query s_j of a segment: its chunk's k text keys and itself.  Lane
-// (hh, c) holds dims 8c .. 8c+7 of head hh of a group of four.
+// (hh, c) holds dims 8c .. 8c+7 of head hh of a group of four.  The key and
+// value rows of a pass (SUM_R rows: 9, one pass, when k <= 8, else 16) are
+// all loaded before any is used, so a pass costs one memory round trip;
+// rows past the chunk are loaded (clamped) and masked.
+template <int SUM_R>
 __device__ void chunk_summary_wave(const CkArgs& a, int64_t item, const ChunkPtrs& p) {
   const int lane = threadIdx.x & 63;
   const int c = lane & 15;
@@ -81,12 +88,24 @@ __device__ void chunk_summary_wave(const CkArgs& a, int64_t item, const ChunkPtr
   if (j >= a1 / (a.k + 1)) return;
   const int t_seg = a0 - a0 / (a.k + 1);
   const int srow = j * (a.k + 1) + a.k;
+  const int nrows = a.k + 1;
   const bf16_t* ckb = static_cast<const bf16_t*>(p.ck) + (static_cast<int64_t>(b) * a.hkv + kvh) * a.slots * D + 8 * c;
   const bf16_t* cvb = static_cast<const bf16_t*>(p.cv) + (static_cast<int64_t>(b) * a.hkv + kvh) * a.slots * D + 8 * c;
   const int64_t kvs = static_cast<int64_t>(a.hkv) * D;
   const bf16_t* skb = static_cast<const bf16_t*>(p.k) + (off - a0) * kvs + kvh * D + 8 * c;
   const bf16_t* svb = static_cast<const bf16_t*>(p.v) + (off - a0) * kvs + kvh * D + 8 * c;
   const bf16_t* qb = static_cast<const bf16_t*>(p.q);
+  // key e of the chunk: text j k + e (the cache's current chunk, slot k - e,
+  // while it precedes the segment; else a segment row), e = k: s_j itself
+  auto kv_offset = [&](int e, bool* in_cache) -> int64_t {
+    if (e == a.k) {
+      *in_cache = false;
+      return static_cast<int64_t>(srow) * kvs;
+    }
+    const int x = j * a.k + e;
+    *in_cache = x < t_seg;
+    return *in_cache ? static_cast<int64_t>(a.k - e) * D : static_cast<int64_t>(x + j) * kvs;
+  };
   for (int hg = 0; hg < a.g; hg += 4) {
     const int hloc = hg + hh;
     const bool hval = hloc < a.g;
@@ -94,37 +113,40 @@ __device__ void chunk_summary_wave(const CkArgs& a, int64_t item, const ChunkPtr
     const int64_t qrow = off + srow - a0;
     const u32x4_t qw = *reinterpret_cast<const u32x4_t*>(qb + (qrow * a.hq + h) * D + 8 * c);
     float m_run = kNegInf, l = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int e = 0; e <= a.k; ++e) {
-      const bf16_t *kp, *vp;
-      if (e == a.k) {
-        kp = skb + static_cast<int64_t>(srow) * kvs;
-        vp = svb + static_cast<int64_t>(srow) * kvs;
-      } else {
-        const int x = j * a.k + e;
-        if (x < t_seg) {  // chunk m, still in the current region
-          kp = ckb + static_cast<int64_t>(a.k - e) * D;
-          vp = cvb + static_cast<int64_t>(a.k - e) * D;
-        } else {
-          kp = skb + static_cast<int64_t>(x + j) * kvs;
-          vp = svb + static_cast<int64_t>(x + j) * kvs;
-        }
+    for (int s0 = 0; s0 < nrows; s0 += SUM_R) {
+      u32x4_t kw[SUM_R], vw[SUM_R];
+#pragma unroll
+      for (int rr = 0; rr < SUM_R; ++rr) {
+        bool in_cache;
+        const int64_t o_ = kv_offset(min(s0 + rr, nrows - 1), &in_cache);
+        kw[rr] = *reinterpret_cast<const u32x4_t*>((in_cache ? ckb : skb) + o_);
+        vw[rr] = *reinterpret_cast<const u32x4_t*>((in_cache ? cvb : svb) + o_);
       }
-      const u32x4_t kw = *reinterpret_cast<const u32x4_t*>(kp);
-      const u32x4_t vw = *reinterpret_cast<const u32x4_t*>(vp);
-      float part = 0.f;
+      float sc[SUM_R];
+      float mx = m_run;
 #pragma unroll
-      for (int w = 0; w < 4; ++w)
-        part = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qw[w]), as_bf16x2(kw[w]), part, false);
-      part = sum16(part);
-      const float sc = part * a.sl;
-      const float mx = fmaxf(m_run, sc);
+      for (int rr = 0; rr < SUM_R; ++rr) {
+        float part = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          part = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qw[w]), as_bf16x2(kw[rr][w]), part, false);
+        part = sum16(part);
+        sc[rr] = s0 + rr < nrows ? part * a.sl : kNegInf;
+        mx = fmaxf(mx, sc[rr]);
+      }
       const float al = m_run == kNegInf ? 0.f : fast_exp2(m_run - mx);
-      const float pr = fast_exp2(sc - mx);
-      l = l * al + pr;
+      l *= al;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        o[2 * w] = o[2 * w] * al + pr * bf_lo(vw[w]);
-        o[2 * w + 1] = o[2 * w + 1] * al + pr * bf_hi(vw[w]);
+      for (int e = 0; e < 8; ++e) o[e] *= al;
+#pragma unroll
+      for (int rr = 0; rr < SUM_R; ++rr) {
+        const float pr = fast_exp2(sc[rr] - mx);
+        l += pr;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          o[2 * w] += pr * bf_lo(vw[rr][w]);
+          o[2 * w + 1] += pr * bf_hi(vw[rr][w]);
+        }
       }
       m_run = mx;
     }
@@ -141,13 +163,6 @@ __device__ void chunk_summary_wave(const CkArgs& a, int64_t item, const ChunkPtr
 
 }  // namespace
 
-// Summary query rows of the segments: a launch of its own, with no LDS, so
-// that these short, latency-bound waves run at full occupancy.
-__global__ void __launch_bounds__(256) prefill_chunk_summary_kernel(CkArgs a, ChunkPtrs p) {
-  const int64_t item = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (item < static_cast<int64_t>(a.batch) * a.hkv * a.max_sum_seg) chunk_summary_wave(a, item, p);
-}
-
 template <int HPW>
 __global__ void __launch_bounds__(256, 2) prefill_chunk_d128_kernel(CkArgs a, ChunkPtrs p) {
   constexpr int PT = 32 * (4 / HPW);
@@ -156,8 +171,26 @@ __global__ void __launch_bounds__(256, 2) prefill_chunk_d128_kernel(CkArgs a, Ch
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n_slots = a.batch * a.hkv * a.n_hg;
   const int bid = blockIdx.x;
-  const int hslot = bid % n_slots;
-  const int tile = a.n_tiles - 1 - bid / n_slots;  // later positions (more keys) first
+  if (bid >= a.n_text_blocks) {  // summary query rows: the shortest work, last
+    const int64_t item = static_cast<int64_t>(bid - a.n_text_blocks) * 4 + wave;
+    if (item < static_cast<int64_t>(a.batch) * a.hkv * a.max_sum_seg) {
+      if (a.k <= 8)
+        chunk_summary_wave<9>(a, item, p);
+      else
+        chunk_summary_wave<16>(a, item, p);
+    }
+    return;
+  }
+  int hslot, t_rev;
+  if (a.xcd_map) {  // blocks go round-robin to the 8 XCDs: one slot's tiles share an L2
+    const int x = bid & 7, s8 = bid >> 3;
+    hslot = (s8 / a.n_tiles) * 8 + x;
+    t_rev = s8 % a.n_tiles;
+  } else {
+    hslot = bid % n_slots;
+    t_rev = bid / n_slots;
+  }
+  const int tile = a.n_tiles - 1 - t_rev;  // later positions (more keys) first
   const int hg = hslot % a.n_hg;
   const int kvh = (hslot / a.n_hg) % a.hkv;
   const int b = hslot / (a.n_hg * a.hkv);
@@ -511,11 +544,11 @@ static hipError_t launch_hpw(const ChunkArgs& c, const ChunkPtrs& p, hipStream_t
   a.total_rows = c.total_rows;
   const int64_t sum_items = static_cast<int64_t>(a.batch) * a.hkv * a.max_sum_seg;
   a.n_sum_blocks = static_cast<int32_t>((sum_items + 3) / 4);
-  const int64_t blocks = static_cast<int64_t>(a.batch) * a.hkv * a.n_hg * a.n_tiles;
+  const int64_t n_slots = static_cast<int64_t>(a.batch) * a.hkv * a.n_hg;
+  a.n_text_blocks = static_cast<int32_t>(n_slots * a.n_tiles);
+  a.xcd_map = (n_slots % 8) == 0 ? 1 : 0;
+  const int64_t blocks = static_cast<int64_t>(a.n_text_blocks) + a.n_sum_blocks;
   hipLaunchKernelGGL(prefill_chunk_d128_kernel<HPW>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, s, a, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.n_sum_blocks == 0) return e;
-  hipLaunchKernelGGL(prefill_chunk_summary_kernel, dim3(static_cast<uint32_t>(a.n_sum_blocks)), dim3(256), 0, s, a, p);
   return hipGetLastError();
 }
 
