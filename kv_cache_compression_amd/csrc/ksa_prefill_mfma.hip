@@ -277,29 +277,6 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_d128_kernel(
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
       qop[ks] = q_valid ? *reinterpret_cast<const bf16x8_t*>(qp + 16 * ks) : bf16x8_t{};
-    if constexpr (QROT) {
-      // text t_qi sits at position qi; dims f = 16 ks + 8 half + j (ks < 4)
-      // and f + 64 are both in this lane
-      const double pos = static_cast<double>(qi);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        u32x4_t lo = __builtin_bit_cast(u32x4_t, qop[ks]), hi = __builtin_bit_cast(u32x4_t, qop[ks + 4]);
-        double fr = half ? a.rope_fr[2 * ks + 1] : a.rope_fr[2 * ks];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          float sn0, cs0, sn1, cs1;
-          rope_sincos(pos, fr, &sn0, &cs0);
-          fr *= a.rope_ratio;
-          rope_sincos(pos, fr, &sn1, &cs1);
-          fr *= a.rope_ratio;
-          const uint32_t x = lo[w], y = hi[w];
-          lo[w] = rope_pair(x, y, false, sn0, cs0, sn1, cs1);
-          hi[w] = rope_pair(y, x, true, sn0, cs0, sn1, cs1);
-        }
-        qop[ks] = __builtin_bit_cast(bf16x8_t, lo);
-        qop[ks + 4] = __builtin_bit_cast(bf16x8_t, hi);
-      }
-    }
   }
 
   // Tile loads: thread owns 16-byte chunk (tid % 16) of rows tid/16 + 16 u
@@ -327,6 +304,7 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_d128_kernel(
   __shared__ __attribute__((aligned(16))) char lds_v1[TILE_BYTES];
   char* const lds_k[2] = {lds_k0, lds_k1};
   char* const lds_v[2] = {lds_v0, lds_v1};
+
   // byte offsets of this thread's 4 rows of tile tt.  Rows past a run's end
   // are read (masked later) or, past the sequence, return zeros through the
   // buffer range check.  When k divides 64 a text tile starts 64 + 64/k rows
@@ -516,6 +494,62 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_d128_kernel(
     load_tile(rsrc_k, lds_k[0], 0);
     load_tile(rsrc_v, lds_v[0], 0);
     load_tile(rsrc_k, lds_k[1], n_total > 1 ? 1 : 0);
+  }
+  if constexpr (QROT) {
+    // Query rotation: text t_qi sits at position qi; dims f = 16 ks + 8 half
+    // + j (ks < 4) and f + 64 are both in this lane.  (sin, cos) of the
+    // angle of (position, f): with four heads per block all waves hold the
+    // same 32 positions, so each thread forms 8 of the 32 x 64 pairs into
+    // the second V buffer (not yet in use: the barrier before the loop
+    // orders these reads before its first load) and every lane reads its
+    // 32; otherwise each lane forms its own.  This runs while the first
+    // tiles are in flight: its barrier waits for LDS writes only.
+    float2* const tab = reinterpret_cast<float2*>(lds_v1);  // [f][position in the block's 32]
+    if constexpr (HPW == 4) {
+      static_assert(64 * 32 * sizeof(float2) <= TILE_BYTES, "the table fits one tile buffer");
+      const int tp = tid & 31, fg = tid >> 5;
+      const double pos = static_cast<double>(iw0 + tp);
+      double fr = a.rope_fr[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) fr = fg == i ? a.rope_fr[i] : fr;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float sn, cs;
+        rope_sincos(pos, fr, &sn, &cs);
+        fr *= a.rope_ratio;
+        tab[(8 * fg + j) * 32 + tp] = make_float2(sn, cs);
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this thread's table writes are done
+      __builtin_amdgcn_s_barrier();
+    }
+    const double pos = static_cast<double>(qi);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      u32x4_t lo = __builtin_bit_cast(u32x4_t, qop[ks]), hi = __builtin_bit_cast(u32x4_t, qop[ks + 4]);
+      double fr = half ? a.rope_fr[2 * ks + 1] : a.rope_fr[2 * ks];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        float sn0, cs0, sn1, cs1;
+        if constexpr (HPW == 4) {
+          const int f = 16 * ks + 8 * half + 2 * w;
+          const float2 e0 = tab[f * 32 + (lane & 31)], e1 = tab[(f + 1) * 32 + (lane & 31)];
+          sn0 = e0.x, cs0 = e0.y, sn1 = e1.x, cs1 = e1.y;
+        } else {
+          rope_sincos(pos, fr, &sn0, &cs0);
+          fr *= a.rope_ratio;
+          rope_sincos(pos, fr, &sn1, &cs1);
+          fr *= a.rope_ratio;
+        }
+        const uint32_t x = lo[w], y = hi[w];
+        lo[w] = rope_pair(x, y, false, sn0, cs0, sn1, cs1);
+        hi[w] = rope_pair(y, x, true, sn0, cs0, sn1, cs1);
+      }
+      qop[ks] = __builtin_bit_cast(bf16x8_t, lo);
+      qop[ks + 4] = __builtin_bit_cast(bf16x8_t, hi);
+    }
+  }
+
+  if (n_total > 0) {
     __syncthreads();
     s_tile(lds_k[0], sa);
     mask_tile(0, sa);
