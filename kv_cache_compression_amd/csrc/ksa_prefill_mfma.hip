@@ -62,19 +62,21 @@ struct MfmaArgs {
   int32_t mode;             // KSA_MODE_*: summaries and text window of text queries
   int32_t W;                // token window of KSA_MODE_SWA
   // Query rotary embedding applied on load (the QROT kernels): frequency f
-  // turns by theta^(-2f/128) radians per position; rope_fr[i] is that rate
-  // in revolutions for f = 8 i, rope_ratio steps f by one.
-  double rope_fr[8];
-  double rope_ratio;
+  // turns by theta^(-2f/128) radians per position; rope_fq[f] is that rate
+  // in revolutions as a 64-bit binary fraction (rate * 2^64, rounded).
+  uint64_t rope_fq[64];
 };
 
-// sin and cos of the angle pos * fr revolutions: the product is reduced to
-// [-1/2, 1/2] revolutions in fp64 (exact up to fp64 rounding for any
-// position an int32 holds), then v_sin_f32 / v_cos_f32, which take their
-// argument in revolutions.
-__device__ __forceinline__ void rope_sincos(double pos, double fr, float* sn, float* cs) {
-  const double x = pos * fr;
-  const float r = static_cast<float>(x - rint(x));
+// sin and cos of position pos at rate fq (a 64-bit fraction of a
+// revolution per position).  pos * fq modulo 2^64 is the angle's fraction
+// of a turn, exact in integers; its top 32 bits, read as a signed number,
+// are the angle in [-1/2, 1/2) revolutions to 2^-32, which v_sin_f32 /
+// v_cos_f32 take directly (their argument is in revolutions).  The rate's
+// rounding adds at most pos * 2^-65 revolutions.
+__device__ __forceinline__ void rope_sincos(uint32_t pos, uint64_t fq, float* sn, float* cs) {
+  const uint32_t lo = static_cast<uint32_t>(fq), hi = static_cast<uint32_t>(fq >> 32);
+  const uint32_t top = __umulhi(lo, pos) + hi * pos;
+  const float r = static_cast<float>(static_cast<int32_t>(top)) * 0x1p-32f;
   *sn = __builtin_amdgcn_sinf(r);
   *cs = __builtin_amdgcn_cosf(r);
 }
@@ -126,20 +128,21 @@ __device__ void summary_rows_wave(const MfmaArgs& a, int64_t item, const bf16_t*
         q + (static_cast<int64_t>(b) * a.L + srow_a) * a.hq * D + static_cast<int64_t>(h) * D + 8 * c);
     if constexpr (QROT) {
       // position of s_j: its chunk's last text token; dims 8c .. 8c+7 pair
-      // with dims 8c +- 64, which lane c ^ 8 of the same 16 holds
-      const double pos = static_cast<double>(j + 1) * a.k - 1;
-      double fr = a.rope_fr[0];
-#pragma unroll
-      for (int i = 1; i < 8; ++i) fr = (c & 7) == i ? a.rope_fr[i] : fr;
+      // with dims 8c +- 64, which lane c ^ 8 of the same 16 holds.  The
+      // wave needs the 64 angles f = 0..63 at one position: lane l forms
+      // angle l and each lane gathers its eight (f = 8 (c % 8) + e) with
+      // ds_bpermute.
+      float sn_l, cs_l;
+      rope_sincos(static_cast<uint32_t>((j + 1) * a.k - 1), a.rope_fq[lane], &sn_l, &cs_l);
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         const uint32_t y = static_cast<uint32_t>(
             __builtin_amdgcn_update_dpp(0, static_cast<int>(qw[w]), 0x128, 0xF, 0xF, false));  // row_ror:8
-        float sn0, cs0, sn1, cs1;
-        rope_sincos(pos, fr, &sn0, &cs0);
-        fr *= a.rope_ratio;
-        rope_sincos(pos, fr, &sn1, &cs1);
-        fr *= a.rope_ratio;
+        const int f0 = 4 * (8 * (c & 7) + 2 * w);  // byte address of lane f
+        const float sn0 = __int_as_float(__builtin_amdgcn_ds_bpermute(f0, __float_as_int(sn_l)));
+        const float cs0 = __int_as_float(__builtin_amdgcn_ds_bpermute(f0, __float_as_int(cs_l)));
+        const float sn1 = __int_as_float(__builtin_amdgcn_ds_bpermute(f0 + 4, __float_as_int(sn_l)));
+        const float cs1 = __int_as_float(__builtin_amdgcn_ds_bpermute(f0 + 4, __float_as_int(cs_l)));
         qw[w] = rope_pair(qw[w], y, c >= 8, sn0, cs0, sn1, cs1);
       }
     }
@@ -508,37 +511,30 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_d128_kernel(
     if constexpr (HPW == 4) {
       static_assert(64 * 32 * sizeof(float2) <= TILE_BYTES, "the table fits one tile buffer");
       const int tp = tid & 31, fg = tid >> 5;
-      const double pos = static_cast<double>(iw0 + tp);
-      double fr = a.rope_fr[0];
-#pragma unroll
-      for (int i = 1; i < 8; ++i) fr = fg == i ? a.rope_fr[i] : fr;
+      const uint32_t pos = static_cast<uint32_t>(iw0 + tp);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         float sn, cs;
-        rope_sincos(pos, fr, &sn, &cs);
-        fr *= a.rope_ratio;
+        rope_sincos(pos, a.rope_fq[8 * fg + j], &sn, &cs);
         tab[(8 * fg + j) * 32 + tp] = make_float2(sn, cs);
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this thread's table writes are done
       __builtin_amdgcn_s_barrier();
     }
-    const double pos = static_cast<double>(qi);
+    const uint32_t pos = static_cast<uint32_t>(qi);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       u32x4_t lo = __builtin_bit_cast(u32x4_t, qop[ks]), hi = __builtin_bit_cast(u32x4_t, qop[ks + 4]);
-      double fr = half ? a.rope_fr[2 * ks + 1] : a.rope_fr[2 * ks];
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
+        const int f = 16 * ks + 8 * half + 2 * w;
         float sn0, cs0, sn1, cs1;
         if constexpr (HPW == 4) {
-          const int f = 16 * ks + 8 * half + 2 * w;
           const float2 e0 = tab[f * 32 + (lane & 31)], e1 = tab[(f + 1) * 32 + (lane & 31)];
           sn0 = e0.x, cs0 = e0.y, sn1 = e1.x, cs1 = e1.y;
         } else {
-          rope_sincos(pos, fr, &sn0, &cs0);
-          fr *= a.rope_ratio;
-          rope_sincos(pos, fr, &sn1, &cs1);
-          fr *= a.rope_ratio;
+          rope_sincos(pos, a.rope_fq[f], &sn0, &cs0);
+          rope_sincos(pos, a.rope_fq[f + 1], &sn1, &cs1);
         }
         const uint32_t x = lo[w], y = hi[w];
         lo[w] = rope_pair(x, y, false, sn0, cs0, sn1, cs1);
@@ -650,13 +646,15 @@ static hipError_t launch_hpw(const PrefillArgs& p, const void* q, const void* k,
   a.W = static_cast<int32_t>(p.window_tokens);
   const int64_t sum_items = static_cast<int64_t>(a.batch) * a.hkv * a.M;
   a.n_sum_blocks = static_cast<int32_t>(((sum_items + 3) / 4 + 7) / 8 * 8);  // keeps text blocks XCD-aligned
-  for (int i = 0; i < 8; ++i) a.rope_fr[i] = 0.0;
-  a.rope_ratio = 0.0;
   const bool qrot = p.rope_theta > 0.0;
-  if (qrot) {
-    constexpr double kTwoPi = 6.283185307179586;
-    for (int i = 0; i < 8; ++i) a.rope_fr[i] = std::pow(p.rope_theta, -16.0 * i / D) / kTwoPi;
-    a.rope_ratio = std::pow(p.rope_theta, -2.0 / D);
+  for (int f = 0; f < 64; ++f) {
+    // theta^(-2f/128) / (2 pi) revolutions per position, below 1/6, as a
+    // 64-bit binary fraction: split so that each part is exact in a double
+    constexpr long double kTwoPi = 6.283185307179586476925286766559L;
+    const long double rate = qrot ? std::pow(static_cast<long double>(p.rope_theta), -2.0L * f / D) / kTwoPi : 0.0L;
+    const long double scaled_hi = std::floor(std::ldexp(rate, 32));
+    const long double rest = std::ldexp(rate, 32) - scaled_hi;  // in [0, 1)
+    a.rope_fq[f] = (static_cast<uint64_t>(scaled_hi) << 32) + static_cast<uint64_t>(std::llround(std::ldexp(rest, 32)));
   }
   const int64_t blocks = a.n_text_blocks + a.n_sum_blocks;
   if (blocks == 0) return hipSuccess;
