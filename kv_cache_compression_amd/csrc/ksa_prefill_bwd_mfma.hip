@@ -293,55 +293,54 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_d128_kernel(
     }
     const char* kl = lds_k[cur];
     const char* vl = lds_v[cur];
-    f32x16_t s[2], dp[2];
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb2][r] = dp[kb2][r] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
-        const int off = (koff0 ^ (ks << 5)) + 32 * ROW_BYTES * kb2;
-        const bf16x8_t kop = *reinterpret_cast<const bf16x8_t*>(kl + off);
-        const bf16x8_t vop = *reinterpret_cast<const bf16x8_t*>(vl + off);
-        s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[ks], s[kb2], 0, 0, 0);
-        dp[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, gop[ks], dp[kb2], 0, 0, 0);
-      }
     // edge tiles: key of (kb2, r) = key0 + 32 kb2 + 8 (r / 4) + 4 half + r % 4
     const bool is_sum = tt < ns;
     const int key0 = is_sum ? tt * BN : t0 + (tt - ns) * BN;
     const bool full = is_sum ? key0 + BN - 1 <= cw0 - a.C - 1 : (key0 >= tlo_w1 && key0 + BN - 1 <= iw0);
-    if (!full) {
-      const int kbase = key0 + 4 * half;
-      const int lo_r = (is_sum ? -1 : tlo) - kbase, hi_r = (is_sum ? smax : qi) - kbase;
+    const int kbase = key0 + 4 * half;
+    const int lo_r = (is_sum ? -1 : tlo) - kbase, hi_r = (is_sum ? smax : qi) - kbase;
+    // the tile's two 32-key halves one after the other: S^T, dP^T and dS^T of
+    // one half, then its dQ^T += K^T dS^T, so that one half's scores are live
+    // at a time (the freed registers let the LDS operand reads run ahead)
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      f32x16_t s, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const int off = (koff0 ^ (ks << 5)) + 32 * ROW_BYTES * kb2;
+        const bf16x8_t kop = *reinterpret_cast<const bf16x8_t*>(kl + off);
+        const bf16x8_t vop = *reinterpret_cast<const bf16x8_t*>(vl + off);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[ks], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, gop[ks], dp, 0, 0, 0);
+      }
+      if (!full) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int off = 32 * kb2 + 8 * (r >> 2) + (r & 3);
-          s[kb2][r] = (off >= lo_r && off <= hi_r) ? s[kb2][r] : kNegInf;
+          s[r] = (off >= lo_r && off <= hi_r) ? s[r] : kNegInf;
         }
-    }
-    // dS^T packed as the B operand of dQ^T += K^T dS^T (keys 16 ks + ...)
-    u32x4_t pw[4];
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
+      }
+      // dS^T packed as the B operand of dQ^T += K^T dS^T (keys 16 ks + ...)
+      u32x4_t pw[2];
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        const float p0 = fast_exp2(fmaf(s[kb2][r], a.sl, nlse2));
-        const float p1 = fast_exp2(fmaf(s[kb2][r + 1], a.sl, nlse2));
-        pw[2 * kb2 + (r >> 3)][(r & 7) >> 1] = pk_bf16(p0 * (dp[kb2][r] - dl), p1 * (dp[kb2][r + 1] - dl));
+        const float p0 = fast_exp2(fmaf(s[r], a.sl, nlse2));
+        const float p1 = fast_exp2(fmaf(s[r + 1], a.sl, nlse2));
+        pw[r >> 3][(r & 7) >> 1] = pk_bf16(p0 * (dp[r] - dl), p1 * (dp[r + 1] - dl));
       }
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, pw[ks]);
+      for (int kk = 0; kk < 2; ++kk) {
+        const int ks = 2 * kb2 + kk;
+        const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, pw[kk]);
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const bf16x4_t lo = lds_read_tr(kl, toff[0][db] + 16 * ROW_BYTES * ks);
-        const bf16x4_t hi = lds_read_tr(kl, toff[1][db] + 16 * ROW_BYTES * ks);
-        const bf16x8_t aop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bop, dqacc[db], 0, 0, 0);
+        for (int db = 0; db < 4; ++db) {
+          const bf16x4_t lo = lds_read_tr(kl, toff[0][db] + 16 * ROW_BYTES * ks);
+          const bf16x4_t hi = lds_read_tr(kl, toff[1][db] + 16 * ROW_BYTES * ks);
+          const bf16x8_t aop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bop, dqacc[db], 0, 0, 0);
+        }
       }
     }
     __syncthreads();
