@@ -191,7 +191,9 @@ __device__ void mla_write_cut(const MlaArgs& a, const int32_t* state, const int3
 static constexpr int kMlaCuCap = 1024;
 
 // Record of one (work item, head): {m (log2 units), l} as two floats, then
-// 512 bf16 of the unnormalised output.
+// 512 bf16 of the unnormalised output.  One bf16 rounding of the partial
+// output before the merge costs the result about what its own bf16 output
+// rounding does, and fp32 records would double the records' HBM traffic.
 constexpr int kMlaRec = 8 + DV * 2;
 
 // Workspace: the records of at most max_items = CUs + batch work items,
