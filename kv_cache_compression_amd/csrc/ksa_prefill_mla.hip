@@ -12,17 +12,20 @@
 // One workgroup of 8 wavefronts per (sequence, augmented row) computes all
 // 128 heads, so each key tile staged in LDS feeds 128 query rows; tiles of
 // 32 keys walk the row's summary run, then its text run (only a run's last
-// tile is partial), loaded straight into LDS with per-lane row addresses
-// from the Eq. (1) map (summary j at row j(k+1)+k, text x at x + x/k).
-// Wave w owns heads 16w .. 16w+15 over the full key and value width:
-// S^T = K Q^T on 16x16x32 bf16 MFMA (two 16-key blocks), and O^T += V^T P^T
-// with V^T read through ds_read_b64_tr_b16 from the same tile in the key
-// order in which the lane holds its probabilities, so no score leaves the
-// wave.  The exponentials of a row use one reference per head (the first
-// tile's maximum), so the 128 output accumulators are never rescaled; a row
-// whose later tiles exceed that reference by more than 2^8 is computed again
-// with its own maximum (found by the first pass).  Rows are taken longest
-// first (text rows from the end of the sequence), summary rows last.
+// tile is partial), loaded straight into LDS, three buffers deep, with
+// per-lane row addresses from the Eq. (1) map (summary j at row j(k+1)+k,
+// text x at x + x/k).  Waves 2p and 2p+1 own heads 32p .. 32p+31: wave
+// 2p+h forms the part of S^T = K Q^T over key columns 288h .. 288h+287 on
+// 32x32x16 bf16 MFMA, the two parts are summed through LDS (the same sum in
+// both waves), both run the same softmax, and wave 2p+h accumulates value
+// columns 256h .. 256h+255 of O^T += V^T P^T, V^T read through
+// ds_read_b64_tr_b16 from the same tile.  Each wave thus holds half of Q
+// and of O, and reads half of each tile per 32 heads, which halves the LDS
+// operand traffic of the full-width 16-head split (the limit there: 544 KB
+// of operand reads per 32-key tile and CU).  The reference maximum moves
+// only when a tile exceeds it by more than 2^8 (the accumulators are then
+// rescaled in place).  Rows are taken longest first (text rows from the end
+// of the sequence), summary rows last.
 #include <type_traits>
 
 #include "ksa_internal.h"
@@ -38,16 +41,11 @@ constexpr int DQK = 576, DV = 512;
 constexpr int HQ = 128;
 constexpr int TK = 32;                  // keys per tile
 constexpr int GRB = DQK * 2;            // bytes per augmented row in HBM: 1152
-// LDS rows are padded to 1184 bytes (74 chunks of 16): 296 dwords, 40 mod
-// the 64 banks, so the 8 rows a half wave reads in a transposing V^T read
-// (8 dwords each) fall on 8 disjoint groups of 8 banks; rows 8 .. 15 of
-// every 16 store their 16-byte chunks pairwise swapped (chunk c at c ^ 1),
-// so the 16 rows of a K operand read (4 dwords each) cover all 64 banks too.
-// (With 1168-byte rows, 36 mod 64, both reads met two-way conflicts.)
-constexpr int RB = GRB + 32;            // 1184
-constexpr int RCH = RB / 16;            // 74
-constexpr int TILE_LDS = 37 * 64 * 16;  // 37888 bytes = 32 x 1184
-static_assert(TILE_LDS == 32 * RB, "a tile fills its buffer exactly");
+constexpr int RB = GRB + 16;            // padded LDS row: 1168 bytes (73 chunks)
+constexpr int RCH = RB / 16;            // 73
+constexpr int TILE_LDS = 37 * 64 * 16;  // 37888 bytes >= 32 x 1168
+constexpr int KPF = 4;                  // K operand reads issued this many MFMAs ahead
+constexpr int VPF = 4;                  // V^T operand reads issued this many MFMAs ahead
 constexpr int NBUF = 3;
 constexpr float kLazy = 8.f;
 
@@ -73,6 +71,9 @@ __global__ void __launch_bounds__(512, 1) prefill_mla_kernel(MlaPrefillArgs a, c
   __shared__ __attribute__((aligned(16))) char lds0[TILE_LDS];
   __shared__ __attribute__((aligned(16))) char lds1[TILE_LDS];
   __shared__ __attribute__((aligned(16))) char lds2[TILE_LDS];
+  // partial S^T exchange between the two waves of a pair: 16 values + 4
+  // padding per lane
+  __shared__ __attribute__((aligned(16))) float xs[8][64][20];
   char* const lds[NBUF] = {lds0, lds1, lds2};
 
   // row of this workgroup: text rows from the last backwards, then summaries
@@ -106,34 +107,37 @@ __global__ void __launch_bounds__(512, 1) prefill_mla_kernel(MlaPrefillArgs a, c
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g4 = lane >> 4;    // lane group: keys 4 g4 .. (and 16 + 4 g4 ..)
-  const int l16 = lane & 15;   // head within the wave's 16
-  const int head = 16 * wave + l16;
+  const int pair = wave >> 1;  // heads 32 pair .. 32 pair + 31
+  const int hf = wave & 1;     // key columns 288 hf .., value columns 256 hf ..
+  const int half = lane >> 5;
+  const int head = 32 * pair + (lane & 31);
   const int64_t qo = (static_cast<int64_t>(b) * a.L + row) * HQ + head;
 
-  // Q^T as the B operand of S^T = K Q^T on 16x16x32 MFMA: column = head
-  // (lane % 16), k-slots d = 32 kd + 8 (lane / 16) + j over all 576 columns.
+  // Q^T (this wave's key-column half) as the B operand of S^T = K Q^T on
+  // 32x32x16 MFMA: column = head (lane % 32), k-slots d = 288 hf + 16 ks + 8 half + j.
   bf16x8_t qop[18];
   {
-    const bf16_t* qp = q + qo * DQK + 8 * g4;
+    const bf16_t* qp = q + qo * DQK + 288 * hf + 8 * half;
 #pragma unroll
-    for (int kd = 0; kd < 18; ++kd) qop[kd] = *reinterpret_cast<const bf16x8_t*>(qp + 32 * kd);
+    for (int ks = 0; ks < 18; ++ks) qop[ks] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * ks);
   }
 
-  // Tile loads: LDS chunk s = 64 (8 i + wave) + lane of a tile (i < 5,
-  // 8 i + wave < 37) is tile row s / 74, stored chunk s % 74, which holds
-  // the row's chunk (s % 74) ^ ((row / 8) % 2); chunks 72 and 73 are LDS
-  // padding and read 32 bytes past the row.
+  // Tile loads: chunk s = 64 (8 i + wave) + lane of a tile (i < 5,
+  // 8 i + wave < 37) is tile row s / 73, 16-byte chunk s % 73 (chunk 72 is
+  // LDS padding and reads 16 bytes past the row).
   const int nld = wave < 5 ? 5 : 4;
   auto trw = [&](int i) { return ((8 * i + wave) * 64 + lane) / RCH; };
-  auto tch = [&](int i) {
-    const int s_ = (8 * i + wave) * 64 + lane;
-    const int r_ = s_ / RCH;
-    return 16 * ((s_ - r_ * RCH) ^ ((r_ >> 3) & 1));
-  };
+  auto tch = [&](int i) { return 16 * (((8 * i + wave) * 64 + lane) % RCH); };
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<bf16_t*>(kx + static_cast<int64_t>(b) * a.L * DQK), static_cast<short>(0), a.L * GRB, 0x00020000);
   auto prefetch = [&](int t, char* buf) __attribute__((always_inline)) {
+    // the per-lane row and chunk of each load are formed here, each time:
+    // kept across the loop they are spilled, and a spill reload waits for
+    // every tile copy in flight
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    auto trw = [&](int i) { return ((8 * i + wave) * 64 + ln) / RCH; };
+    auto tch = [&](int i) { return 16 * (((8 * i + wave) * 64 + ln) % RCH); };
     int vo[5];
     if (t < ns) {
       const int j0 = t * TK;
@@ -158,31 +162,22 @@ __global__ void __launch_bounds__(512, 1) prefill_mla_kernel(MlaPrefillArgs a, c
             rsrc, (__attribute__((address_space(3))) void*)(buf + (8 * i + wave) * 1024), 16, vo[i], 0, 0, 0);
   };
 
-  // O^T over the 512 value columns in 32 blocks of 16: lane holds head
-  // lane % 16, d = 16 db + 4 (lane / 16) + r.
-  f32x4_t oacc[32];
+  // O^T over this wave's 256 value columns in 8 blocks of 32: lane holds
+  // head lane % 32, d = 256 hf + 32 db + 8 (r / 4) + 4 half + r % 4.
+  f32x16_t oacc[8];
   float l_run = 0.f;
-  // One exponent reference per head for the whole row, so the output
-  // accumulators are never rescaled: the first pass takes the maximum of the
-  // first tile; if a later tile exceeds it by more than 2^8, the row is
-  // computed again with the row's maximum, which the first pass found.
-  float m_ref = kNegInf, m_all = kNegInf;
-  bool over = false;
-  __shared__ int restart;
-  if (tid == 0) restart = 0;
+  float m_ref = kNegInf;
   const uint32_t one2 = 0x3f803f80u;
-  // K operand (A of 16x16x32): key row lane % 16 (+16), d = 32 kd + 8 (lane / 16) + j
-  // (chunk 4 kd + g4, stored at 4 kd + (g4 ^ 1) in rows 8 .. 15 of 16)
-  const int krow_off = l16 * RB + 16 * (g4 ^ ((l16 >> 3) & 1));
-  // V^T operand (A): in 16-lane group g4, lane (4 rr + c4) points at key row
-  // 4 g4 + rr (+16 for the upper k-slots) and d = 16 db + 4 c4; the
-  // transposing read gives lane i V[4 keys][d = 16 db + i % 16].  The k-slot
-  // order {4 g4 .. 4 g4 + 3, 16 + 4 g4 .. 16 + 4 g4 + 3} is the order in which
-  // the lane holds its probabilities, so P needs no exchange.
-  const int rr = l16 >> 2, c4 = l16 & 3;
-  const int vrow_off = (4 * g4 + rr) * RB + 16 * ((c4 >> 1) ^ ((g4 >> 1) & 1)) + 8 * (c4 & 1);
+  // K operand: row = key lane % 32, bytes 576 hf + 32 ks + 16 half.
+  const int krow_off = (lane & 31) * RB + 16 * half + 576 * hf;
+  // V^T operand: in 16-lane group G, lane (4 rr + c4) reads key row
+  // 4 (G / 2) + rr (+ 8 for the second half of the k-slots) and d =
+  // 256 hf + 32 db + 16 (G % 2) + 4 c4; the transposing read gives lane i
+  // V[4 keys][d = 256 hf + 32 db + i % 32].
+  const int G = lane >> 4, l16 = lane & 15, rr = l16 >> 2, c4 = l16 & 3;
+  const int vrow_off = (4 * (G >> 1) + rr) * RB + 2 * (16 * (G & 1) + 4 * c4) + 512 * hf;
 
-  auto tile_step = [&](auto cur_c, int t, bool first_pass) __attribute__((always_inline)) {
+  auto tile_step = [&](auto cur_c, int t) __attribute__((always_inline)) {
     constexpr int cur = decltype(cur_c)::value;
     if (t + 1 < ntile) {
       if (wave < 5)
@@ -193,90 +188,113 @@ __global__ void __launch_bounds__(512, 1) prefill_mla_kernel(MlaPrefillArgs a, c
       __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
     }
     wg_barrier();
-    // tile t + 2 goes into the buffer of tile t - 1 (released by the barrier)
-    if (t + 2 < ntile) prefetch(t + 2, lds[(cur + 2) % NBUF]);
     const char* kl = lds[cur];
-    // ---- S^T = K Q^T: two 16-key blocks x 16 heads, two chains each ----
-    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    // ---- this wave's half of S^T = K Q^T (keys x heads, 32 x 32) ----
+    f32x16_t s;
 #pragma unroll
-    for (int kd = 0; kd < 18; ++kd) {
-      const bf16x8_t k0 = *reinterpret_cast<const bf16x8_t*>(kl + krow_off + 64 * kd);
-      const bf16x8_t k1 = *reinterpret_cast<const bf16x8_t*>(kl + krow_off + 16 * RB + 64 * kd);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qop[kd], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qop[kd], s1, 0, 0, 0);
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+    bf16x8_t kring[KPF];
+#pragma unroll
+    for (int i = 0; i < KPF; ++i) kring[i] = *reinterpret_cast<const bf16x8_t*>(kl + krow_off + 32 * i);
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) {
+      const bf16x8_t kop = kring[ks % KPF];
+      if (ks + KPF < 18) kring[ks % KPF] = *reinterpret_cast<const bf16x8_t*>(kl + krow_off + 32 * (ks + KPF));
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[ks], s, 0, 0, 0);
     }
-    float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-    // keys of the tile: 16 (e / 4) + 4 g4 + e % 4 < valid
+#pragma unroll
+    for (int r = 0; r < 16; r += 4)
+      *reinterpret_cast<f32x4_t*>(&xs[wave][lane][r]) = (f32x4_t){s[r], s[r + 1], s[r + 2], s[r + 3]};
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // exchange written (lgkmcnt(0)); loads stay in flight
+    wg_barrier();
+    {
+      f32x4_t part[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) part[r] = *reinterpret_cast<const f32x4_t*>(&xs[wave ^ 1][lane][4 * r]);
+      // the same sum in both waves of the pair: a + b == b + a exactly
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = hf == 0 ? s[r] + part[r >> 2][r & 3] : part[r >> 2][r & 3] + s[r];
+    }
+    // tile t + 2 goes into the buffer of tile t - 1 (released by the barrier
+    // at the top of this step); issued after the exchange reads
+    if (t + 2 < ntile) prefetch(t + 2, lds[(cur + 2) % NBUF]);
+    // ---- softmax: lane = head, registers = keys 8 (r/4) + 4 half + r%4 ----
     const int valid = t < ns ? sn - t * TK : x_last - (t0 + (t - ns) * TK) + 1;
     if (valid < TK) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sv[e] = (16 * (e >> 2) + 4 * g4 + (e & 3)) < valid ? sv[e] : kNegInf;
+      for (int r = 0; r < 16; ++r)
+        s[r] = (8 * (r >> 2) + 4 * half + (r & 3)) < valid ? s[r] : kNegInf;
     }
     float tmax = kNegInf;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) tmax = fmaxf(tmax, sv[e]);
-    tmax = with_upper_half_max(with_row_pair_max(tmax)) * a.sl;
-    if (first_pass) {
-      if (t == 0) m_ref = tmax;
-      m_all = fmaxf(m_all, tmax);
-      over = over || tmax > m_ref + kLazy;
+    for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[r]);
+    tmax = with_upper_half_max(tmax) * a.sl;
+    if (__any(tmax > m_ref + kLazy)) {
+      const float m_new = fmaxf(m_ref, tmax);
+      const float alpha = m_ref == kNegInf ? 0.f : fast_exp2(m_ref - m_new);
+      m_ref = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
     }
     const float nm = -m_ref;
-    u32x4_t pw;
+    u32x4_t pw[2];
 #pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      const uint32_t w = pk_bf16(fast_exp2(fmaf(sv[e], a.sl, nm)), fast_exp2(fmaf(sv[e + 1], a.sl, nm)));
-      pw[e >> 1] = w;
-      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), __builtin_bit_cast(bf16x2_t, one2),
-                                              l_run, false);
+    for (int r = 0; r < 16; r += 2) {
+      const uint32_t w = pk_bf16(fast_exp2(fmaf(s[r], a.sl, nm)), fast_exp2(fmaf(s[r + 1], a.sl, nm)));
+      pw[r >> 3][(r & 7) >> 1] = w;
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w),
+                                              __builtin_bit_cast(bf16x2_t, one2), l_run, false);
     }
-    const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, pw);
-    // ---- O^T += V^T P^T over 32 blocks of 16 value columns ----
+    // ---- this wave's half of O^T += V^T P^T (V = first 512 key columns) ----
+    {
+      auto vread = [&](int i) __attribute__((always_inline)) {
+        const int off = vrow_off + 16 * (i >> 3) * RB + 64 * (i & 7);
+        const bf16x4_t lo = lds_read_tr(kl, off);
+        const bf16x4_t hi = lds_read_tr(kl, off + 8 * RB);
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+      bf16x8_t vring[VPF];
 #pragma unroll
-    for (int db = 0; db < 32; ++db) {
-      const int off = vrow_off + 32 * db;
-      const bf16x4_t lo = lds_read_tr(kl, off);
-      const bf16x4_t hi = lds_read_tr(kl, off + 16 * RB);
-      const bf16x8_t vop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop, oacc[db], 0, 0, 0);
+      for (int i = 0; i < VPF; ++i) vring[i] = vread(i);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {  // i = 8 ks + db
+        const bf16x8_t vop = vring[i % VPF];
+        if (i + VPF < 16) vring[i % VPF] = vread(i + VPF);
+        const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, pw[i >> 3]);
+        oacc[i & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop, oacc[i & 7], 0, 0, 0);
+      }
     }
   };
-  for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-    for (int db = 0; db < 32; ++db)
+  for (int db = 0; db < 8; ++db)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) oacc[db][r] = 0.f;
-    l_run = 0.f;
-    const bool first_pass = pass == 0;
-    if (!first_pass) m_ref = m_all;
-    if (ntile > 0) prefetch(0, lds[0]);
-    if (ntile > 1) prefetch(1, lds[1]);
-    for (int t = 0; t < ntile; t += 3) {
-      tile_step(std::integral_constant<int, 0>(), t, first_pass);
-      if (t + 1 < ntile) tile_step(std::integral_constant<int, 1>(), t + 1, first_pass);
-      if (t + 2 < ntile) tile_step(std::integral_constant<int, 2>(), t + 2, first_pass);
-    }
-    __builtin_amdgcn_s_waitcnt(0x0070);  // no LDS write in flight
-    if (!first_pass) break;
-    // one decision for the workgroup (the tiles are shared); the barrier also
-    // releases the tile buffers for a second pass
-    if (__any(over) && lane == 0) restart = 1;
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-    wg_barrier();
-    if (!restart) break;
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+  if (ntile > 0) prefetch(0, lds[0]);
+  if (ntile > 1) prefetch(1, lds[1]);
+  for (int t = 0; t < ntile; t += 3) {
+    tile_step(std::integral_constant<int, 0>(), t);
+    if (t + 1 < ntile) tile_step(std::integral_constant<int, 1>(), t + 1);
+    if (t + 2 < ntile) tile_step(std::integral_constant<int, 2>(), t + 2);
   }
+  __builtin_amdgcn_s_waitcnt(0x0070);  // no LDS write in flight
 
-  const float l_tot = with_upper_half_sum(with_row_pair_sum(l_run));
+  const float l_tot = with_upper_half_sum(l_run);
   const float inv = 1.f / l_tot;
-  bf16_t* op = out + qo * DV + 4 * g4;
+  bf16_t* op = out + qo * DV + 256 * hf;
 #pragma unroll
-  for (int db = 0; db < 32; ++db) {
-    u32x2_t w;
-    w.x = pk_bf16(oacc[db][0] * inv, oacc[db][1] * inv);
-    w.y = pk_bf16(oacc[db][2] * inv, oacc[db][3] * inv);
-    *reinterpret_cast<u32x2_t*>(op + 16 * db) = w;
-  }
-  if (lse && g4 == 0)
+  for (int db = 0; db < 8; ++db)
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const int d = 32 * db + 8 * qq + 4 * half;
+      u32x2_t w;
+      w.x = pk_bf16(oacc[db][4 * qq + 0] * inv, oacc[db][4 * qq + 1] * inv);
+      w.y = pk_bf16(oacc[db][4 * qq + 2] * inv, oacc[db][4 * qq + 3] * inv);
+      *reinterpret_cast<u32x2_t*>(op + d) = w;
+    }
+  if (lse && half == 0 && hf == 0)
     lse[(static_cast<int64_t>(b) * HQ + head) * a.L + row] = (m_ref + log2f(l_tot)) * kLn2;
 }
 

@@ -76,9 +76,9 @@ def test_mla_prefill_late_large_scores():
     """The 64 rotary key columns (not part of V) of the second half of the
     sequence are 300x larger, so for half of the rows a later key tile's
     maximum exceeds the first tile's by more than 2^127: exponentials taken
-    against the first tile's maximum would overflow, and those rows must take
-    the second pass with the row's own maximum.  Values and normalisers
-    against the oracle."""
+    against the first tile's maximum would overflow, so the kernel must move
+    its reference maximum and rescale what it has accumulated.  Values and
+    normalisers against the oracle."""
     dev = _dev()
     n, k, C = 400, 8, 3
     L = O.augmented_len(n, k)

@@ -1,7 +1,7 @@
 """GPU parity on inputs that force the kernels' deferred rescale.
 
 The MFMA prefill kernels (one-shot and chunked, d = 128) and the absorbed-MLA
-decode keep one exponent reference per query row and move it only when a
+decode and prefill keep one exponent reference per query row and move it only when a
 later key tile's maximum exceeds it by more than 8 (log2 units); O and the
 row sum are then multiplied by 2^(old - new).  With N(0,1) inputs a later
 tile practically never beats the first by that much, so these tests build
@@ -266,3 +266,36 @@ def test_decode_mla_forced_rescale_ragged_batch(J):
         ref, rl = O.decode_attention(q[b].double().numpy(), kn, None, n, k, C, scale, "t", dv=MLA_DV)
         _compare(_np(out[b]), _np(lse[b]), ref, rl, f"MLA ragged b={b} J={J}")
     assert ksa.ksa_cache_read_errors(cache) == [0] * B
+
+
+# ------------------------------------------------------------ MLA prefill --
+
+
+@pytest.mark.parametrize("J", [10.0, 150.0])
+def test_prefill_mla_forced_rescale(J):
+    """Absorbed-MLA prefill: summaries s_40 and s_70 are lifted, so every
+    text row of chunk >= 45 meets a lifted key in the second (or a later)
+    32-key tile of its summary run, after a whole tile at the old level, and
+    must move its reference and rescale what it holds.  All rows against the
+    oracle."""
+    dev = _dev()
+    n, k, C = 803, 8, 4
+    L = O.augmented_len(n, k)
+    lifted = [O.summary_row(40, k), O.summary_row(70, k)]
+    kx, u, scale = _mla_inputs(n, k, J, lifted, 71)
+    g = ksa_synth.gen(72)
+    q = (u + 0.3 * ksa_synth.normal((1, L, MLA_HQ, MLA_DQK), torch.float32, g)).to(torch.bfloat16)
+    kn = kx[0].double().numpy()
+    # the lifted keys beat every other key by more than 2^8 for a text row
+    # late in the sequence
+    row = L - 2
+    s = (kn[:, 0] @ q[0, row].double().numpy().T) * scale * LOG2E   # [keys, heads]
+    others = np.delete(s, lifted, axis=0).max(0)
+    assert (s[lifted[0]] - others).min() > 8.0
+    p = ksa.Params(k, C, MLA_HQ, 1, MLA_DQK, MLA_DV, torch.bfloat16, v_is_k_prefix=True)
+    lse = torch.empty((1, MLA_HQ, L), dtype=torch.float32, device=dev)
+    print(f"MLA prefill, lift {J}", flush=True)
+    out = ksa.ksa_prefill_attn(p, q.to(dev), kx.to(dev), None, n, lse=lse)
+    torch.cuda.synchronize()
+    ref, rl = O.ksa_attention(q[0].double().numpy(), kn, None, n, k, C, scale, dv=MLA_DV)
+    _compare(_np(out[0]), _np(lse[0]), ref, rl, f"MLA prefill J={J}")
