@@ -420,6 +420,16 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_d128_kernel(
     cs0 = div_k(a, key0);
     cs1 = min(a.M - 1, div_k(a, xl));
   }
+  // uniform over the workgroup: kept in scalar registers
+  b = __builtin_amdgcn_readfirstlane(b);
+  kvh = __builtin_amdgcn_readfirstlane(kvh);
+  key0 = __builtin_amdgcn_readfirstlane(key0);
+  u = __builtin_amdgcn_readfirstlane(u);
+  nkeys = __builtin_amdgcn_readfirstlane(nkeys);
+  qt0 = __builtin_amdgcn_readfirstlane(qt0);
+  qt1 = __builtin_amdgcn_readfirstlane(qt1);
+  cs0 = __builtin_amdgcn_readfirstlane(cs0);
+  cs1 = __builtin_amdgcn_readfirstlane(cs1);
   const int ntq = (qt1 - qt0 + BN - 1) / BN;
   const int nts = cs1 >= cs0 ? (cs1 - cs0 + BN) / BN : 0;
   const int per_head = ntq + nts;
@@ -461,14 +471,11 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_d128_kernel(
   // Q / dO tiles: 64 rows of one query head, rows gathered by the Eq. 1 map.
   const int qhs = a.hq * D;  // elements per augmented row
   const int QRB = qhs * 2;
-  const int ld_chunk = tid & 15;
-  const int ld_row = tid >> 4;
-  const int chunk16 = 16 * (ld_chunk ^ lds_swz(ld_row));
   __shared__ __attribute__((aligned(16))) char lds_q0[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char lds_q1[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char lds_g0[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char lds_g1[TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) float lds_st[2][2][BN];  // [buffer][lse2, delta][row]
+  __shared__ __attribute__((aligned(16))) float lds_st[2][2][BN];  // [buffer][lse, delta][row]
   char* const lds_q[2] = {lds_q0, lds_q1};
   char* const lds_g[2] = {lds_g0, lds_g1};
   const int64_t qbase = static_cast<int64_t>(b) * a.L * qhs;
@@ -481,7 +488,14 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_d128_kernel(
     *i0 = *sq ? cs0 + (r - ntq) * BN : qt0 + r * BN;
   };
   auto row_of = [&](bool sq, int idx) { return sq ? summary_row(idx, a.k) : trow(a, idx); };
-  auto load_tile = [&](char* qb, char* gb, int it, float* st_regs) {
+  auto load_tile = [&](char* qb, char* gb, int it, float* st_buf) {
+    // the thread's row and chunk are formed here, each time: kept across the
+    // loop they are spilled, and a spill reload waits for every tile copy in
+    // flight, the next tile's included
+    int t_ = tid;
+    asm volatile("" : "+v"(t_));
+    const int lrow = t_ >> 4;
+    const int lchunk16 = 16 * ((t_ & 15) ^ lds_swz(lrow));
     int h, i0;
     bool sq;
     tile_of(it, &h, &sq, &i0);
@@ -493,19 +507,30 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_d128_kernel(
         const_cast<bf16_t*>(dout + qbase + hoff), static_cast<short>(0), (a.L * qhs - hoff) * 2, 0x00020000);
 #pragma unroll
     for (int uu = 0; uu < 4; ++uu) {
-      const int idx = min(i0 + ld_row + 16 * uu, last);
-      const int vo = static_cast<int>(__umul24(static_cast<uint32_t>(row_of(sq, idx)), QRB)) + chunk16;
+      const int idx = min(i0 + lrow + 16 * uu, last);
+      const int vo = static_cast<int>(__umul24(static_cast<uint32_t>(row_of(sq, idx)), QRB)) + lchunk16;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rq, (__attribute__((address_space(3))) void*)(qb + (64 * wave + 256 * uu) * 16), 16, vo, 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rg, (__attribute__((address_space(3))) void*)(gb + (64 * wave + 256 * uu) * 16), 16, vo, 0, 0, 0);
     }
-    // statistics of the 64 rows: threads 0..63 lse, 64..127 delta
-    if (tid < 2 * BN) {
-      const int rr = tid & (BN - 1);
-      const int idx = min(i0 + rr, last);
-      const int64_t so = (static_cast<int64_t>(b) * a.hq + h) * a.L + row_of(sq, idx);
-      *st_regs = tid < BN ? lse[so] * kLog2e : delta[so];
+    // statistics of the 64 rows straight into LDS, like the tiles: wave 0
+    // the natural-log normaliser, wave 1 delta (no register holds them
+    // across the loop, and the tile's barrier covers them)
+    if (wave < 2) {
+      const int64_t head_row0 = (static_cast<int64_t>(b) * a.hq + h) * a.L;
+      const int vo = row_of(sq, min(i0 + (t_ & (BN - 1)), last)) * 4;
+      if (wave == 0) {
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(lse + head_row0), static_cast<short>(0), a.L * 4, 0x00020000);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(st_buf), 4, vo, 0,
+                                                 0, 0);
+      } else {
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(delta + head_row0), static_cast<short>(0), a.L * 4, 0x00020000);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(st_buf + BN), 4, vo,
+                                                 0, 0, 0);
+      }
     }
   };
 
@@ -532,8 +557,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_d128_kernel(
 
   auto iter = [&](auto cur_c, int it) __attribute__((always_inline)) {
     constexpr int cur = decltype(cur_c)::value;
-    float st_next = 0.f;
-    if (it + 1 < n_total) load_tile(lds_q[cur ^ 1], lds_g[cur ^ 1], it + 1, &st_next);
+    if (it + 1 < n_total) load_tile(lds_q[cur ^ 1], lds_g[cur ^ 1], it + 1, &lds_st[cur ^ 1][0][0]);
     int h, i0;
     bool sq;
     tile_of(it, &h, &sq, &i0);
@@ -581,7 +605,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_d128_kernel(
       for (int r4 = 0; r4 < 4; ++r4) {
         const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(st + 32 * blk + 8 * r4 + 4 * half);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) p[4 * r4 + e] = fast_exp2(s[4 * r4 + e] * a.sl - l4[e]);
+        for (int e = 0; e < 4; ++e) p[4 * r4 + e] = fast_exp2(s[4 * r4 + e] * a.sl - l4[e] * kLog2e);
       }
       f32x16_t dp;
 #pragma unroll
@@ -626,14 +650,11 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_d128_kernel(
         }
       }
     }
-    if (it + 1 < n_total && tid < 2 * BN) lds_st[cur ^ 1][tid >> 6][tid & (BN - 1)] = st_next;
     __syncthreads();
   };
 
   if (n_total > 0) {
-    float st0 = 0.f;
-    load_tile(lds_q[0], lds_g[0], 0, &st0);
-    if (tid < 2 * BN) lds_st[0][tid >> 6][tid & (BN - 1)] = st0;
+    load_tile(lds_q[0], lds_g[0], 0, &lds_st[0][0][0]);
     __syncthreads();
   }
   for (int it = 0; it < n_total; it += 2) {
