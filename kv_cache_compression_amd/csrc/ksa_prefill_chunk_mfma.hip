@@ -42,7 +42,7 @@ constexpr int SLOT_BYTES = ROW_BYTES; // one (slot, kv head) row of the cache
 
 struct CkArgs {
   int32_t batch, k, C, hq, hkv, g, n_hg, n_tiles;
-  uint32_t divk_m, divk_l;
+  uint32_t divk_m, divk_l, divc_m, divc_l;
   float sl;
   int32_t slots, sum0;  // cache slots per (sequence, kv head); first summary slot
   int32_t max_rows, max_sum_seg, n_sum_blocks, n_text_blocks, xcd_map;
@@ -57,7 +57,8 @@ __device__ __forceinline__ int32_t text_slot(const CkArgs& a, int32_t x, int32_t
   const int32_t cx = div_k(a, x);
   const int32_t ox = x - cx * a.k;
   if (cx == m) return a.k - ox;
-  return 1 + a.k + (a.C > 0 ? cx % a.C : 0) * a.k + (a.k - 1 - ox);
+  const int32_t ring = a.C > 0 ? cx - a.C * fast_div_apply(cx, a.divc_m, a.divc_l) : 0;
+  return 1 + a.k + ring * a.k + (a.k - 1 - ox);
 }
 
 // Summary query s_j of a segment: its chunk's k text keys and itself.  Lane
@@ -284,30 +285,58 @@ __global__ void __launch_bounds__(256, 2) prefill_chunk_d128_kernel(CkArgs a, Ch
     }
     return d;
   };
-  // a tile of K (is_v false) or V into buf, straight to LDS
-  auto load_tile = [&](bool is_v, char* buf, const TileDesc& d) {
-    const int run = d.run, key0 = d.key0, kend = d.kend;
+  // Where a tile's 64 rows live: the source (cache or segment), a uniform
+  // byte offset and one per-lane offset per 16-row group.  Rows past the
+  // run's end repeat its last row, so V stays finite under the masked P = 0.
+  // Formed once per tile for its K load and kept for its V load a step later.
+  struct TileAddr {
     int vo[4];
+    int so;
+    bool cache;
+  };
+  auto tile_addr = [&](const TileDesc& d) {
+    TileAddr t;
+    const int lim = d.kend - 1 - d.key0;  // the run's last row within the tile
+    t.cache = d.run == 0 || d.run == 2;
+    if (d.run < 2) {
+      // summaries: slot sum0 + j in the cache, row j (k+1) + k - a0 in the
+      // segment, both affine in j
+      const int stride = d.run == 0 ? SLOT_BYTES : (a.k + 1) * RB;
+      t.so = d.run == 0 ? (a.sum0 + d.key0) * SLOT_BYTES : (d.key0 * (a.k + 1) + a.k - a0) * RB;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        t.vo[u] = static_cast<int>(__umul24(static_cast<uint32_t>(min(ld_row + 16 * u, lim)), stride)) + chunk16;
+    } else if (d.run == 3) {
+      // segment text x = key0 + xl at row x + x / k - a0, where
+      // x / k = key0 / k + (key0 mod k + xl) / k
+      const int q0 = div_k(a, d.key0), r0 = d.key0 - q0 * a.k;
+      t.so = (d.key0 + q0 - a0) * RB;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int xl = min(ld_row + 16 * u, lim);
+        t.vo[u] = static_cast<int>(__umul24(static_cast<uint32_t>(xl + div_k(a, r0 + xl)), RB)) + chunk16;
+      }
+    } else {
+      t.so = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        t.vo[u] = text_slot(a, d.key0 + min(ld_row + 16 * u, lim), m) * SLOT_BYTES + chunk16;
+    }
+    t.so = __builtin_amdgcn_readfirstlane(t.so);  // the load's scalar offset
+    return t;
+  };
+  // a tile of K (is_v false) or V into buf, straight to LDS
+  auto load_tile = [&](bool is_v, char* buf, const TileAddr& t) {
+    const __amdgpu_buffer_rsrc_t rs = t.cache ? (is_v ? rc_v : rc_k) : (is_v ? rs_v : rs_k);
+    const int so = t.so;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int x = min(key0 + ld_row + 16 * u, kend - 1);
-      int o;
-      if (run == 0)
-        o = (a.sum0 + x) * SLOT_BYTES;
-      else if (run == 1)
-        o = static_cast<int>(__umul24(static_cast<uint32_t>(x * (a.k + 1) + a.k - a0), RB));
-      else if (run == 2)
-        o = text_slot(a, x, m) * SLOT_BYTES;
-      else
-        o = static_cast<int>(__umul24(static_cast<uint32_t>(trow(a, x) - a0), RB));
-      vo[u] = o + chunk16;
-    }
-    const bool cache = run == 0 || run == 2;
-    const __amdgpu_buffer_rsrc_t rs = cache ? (is_v ? rc_v : rc_k) : (is_v ? rs_v : rs_k);
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
+      // offsets go to the builtin as plain ints: handed a struct member
+      // directly, hipcc's host pass emits no launch stub for the kernel
+      const int vo = t.vo[u];
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (__attribute__((address_space(3))) void*)(buf + (64 * wave + 256 * u) * 16), 16, vo[u], 0, 0, 0);
+          rs, (__attribute__((address_space(3))) void*)(buf + (64 * wave + 256 * u) * 16), 16, vo, so, 0, 0);
+    }
   };
 
   f32x16_t oacc[4];
@@ -390,6 +419,7 @@ __global__ void __launch_bounds__(256, 2) prefill_chunk_d128_kernel(CkArgs a, Ch
   float m_cur = kNegInf, m_nxt = kNegInf;
   bool grow = false;
   TileDesc d1;  // tile tt + 1 (clamped to the last), carried between iterations
+  TileAddr t1;  // its rows
   auto iter = [&](auto cur_c, int tt, f32x16_t* s_cur, f32x16_t* s_nxt) __attribute__((always_inline)) {
     constexpr int cur = decltype(cur_c)::value;
     const int last = n_total - 1;
@@ -404,8 +434,9 @@ __global__ void __launch_bounds__(256, 2) prefill_chunk_d128_kernel(CkArgs a, Ch
     m_cur = m_nxt;
     // LDS holds K_{tt+1} and V_tt; V_{tt+1} and K_{tt+2} replace V_{tt-1}, K_tt
     const TileDesc d2 = tile_run(tt + 2 < last ? tt + 2 : last);
-    load_tile(true, lds_v[cur ^ 1], d1);
-    load_tile(false, lds_k[cur], d2);
+    load_tile(true, lds_v[cur ^ 1], t1);
+    const TileAddr t2 = tile_addr(d2);
+    load_tile(false, lds_k[cur], t2);
     s_tile(lds_k[cur ^ 1], s_nxt);
     const float nm = m_cur == kNegInf ? 0.f : -m_cur;
     u32x4_t pw[4];
@@ -430,6 +461,7 @@ __global__ void __launch_bounds__(256, 2) prefill_chunk_d128_kernel(CkArgs a, Ch
     grow = __any(tmax > m_cur + kLazyRescale);
     m_nxt = grow ? fmaxf(m_cur, tmax) : m_cur;
     d1 = d2;
+    t1 = t2;
     __syncthreads();
   };
 
@@ -438,9 +470,11 @@ __global__ void __launch_bounds__(256, 2) prefill_chunk_d128_kernel(CkArgs a, Ch
   {
     const TileDesc d0 = tile_run(0);
     d1 = tile_run(n_total > 1 ? 1 : 0);
-    load_tile(false, lds_k[0], d0);
-    load_tile(true, lds_v[0], d0);
-    load_tile(false, lds_k[1], d1);
+    const TileAddr t0a = tile_addr(d0);
+    t1 = tile_addr(d1);
+    load_tile(false, lds_k[0], t0a);
+    load_tile(true, lds_v[0], t0a);
+    load_tile(false, lds_k[1], t1);
     __syncthreads();
     s_tile(lds_k[0], sa);
     mask_tile(d0, sa);
@@ -519,7 +553,7 @@ bool prefill_chunk_mfma_supported(const ChunkArgs& a, int32_t dtype) {
   return dtype == KSA_DTYPE_BF16 && a.dqk == D && a.dv == D && !a.v_is_k_prefix &&
          (g == 1 || g == 2 || g % 4 == 0) && a.slots * SLOT_BYTES < (int64_t(1) << 31) &&
          a.total_rows * a.hkv * D * 2 < (int64_t(1) << 31) && a.total_rows * a.hq * D < (int64_t(1) << 31) &&
-         max_len < (int64_t(1) << 24);
+         max_len < (int64_t(1) << 24) && (a.k + 1) * static_cast<int64_t>(a.hkv) * D * 2 < (int64_t(1) << 24);
 }
 
 template <int HPW>
@@ -536,6 +570,7 @@ static hipError_t launch_hpw(const ChunkArgs& c, const ChunkPtrs& p, hipStream_t
   // text tokens of a segment <= its rows; one more tile for the alignment
   a.n_tiles = static_cast<int32_t>((c.max_rows + PT - 1) / PT + 1);
   fast_div(static_cast<uint32_t>(a.k), &a.divk_m, &a.divk_l);
+  fast_div(static_cast<uint32_t>(a.C > 0 ? a.C : 1), &a.divc_m, &a.divc_l);
   a.sl = c.scale * kLog2e;
   a.slots = static_cast<int32_t>(c.slots);
   a.sum0 = 1 + a.k + a.C * a.k;
