@@ -272,17 +272,18 @@ __global__ void __launch_bounds__(256, 2) prefill_chunk_d128_kernel(CkArgs a, Ch
   struct TileDesc {
     int run, key0, kend;
   };
+  // tile tt of run r starts at key tt BN + shift_r and ends its run at
+  // kend_r: sums of steps taken at the run boundaries, no branches
+  const int dsh1 = m - n0 * BN, dsh2 = t0 - n01 * BN - dsh1, dsh3 = s3 - n012 * BN - dsh1 - dsh2;
+  const int dke1 = sn - e0, dke2 = e2 - sn, dke3 = p_last + 1 - e2;
   auto tile_run = [&](int tt) {
     TileDesc d;
-    if (tt < n0) {
-      d.run = 0; d.key0 = tt * BN; d.kend = e0;
-    } else if (tt < n01) {
-      d.run = 1; d.key0 = m + (tt - n0) * BN; d.kend = sn;
-    } else if (tt < n012) {
-      d.run = 2; d.key0 = t0 + (tt - n01) * BN; d.kend = e2;
-    } else {
-      d.run = 3; d.key0 = s3 + (tt - n012) * BN; d.kend = p_last + 1;
-    }
+    const int r1 = -static_cast<int>(tt >= n0), r2 = -static_cast<int>(tt >= n01), r3 = -static_cast<int>(tt >= n012);
+    // wave-uniform by construction; said so, or hipcc may treat the run's
+    // buffer resource as per-lane and loop over its values
+    d.run = __builtin_amdgcn_readfirstlane(-(r1 + r2 + r3));
+    d.key0 = __builtin_amdgcn_readfirstlane(tt * BN + (r1 & dsh1) + (r2 & dsh2) + (r3 & dsh3));
+    d.kend = __builtin_amdgcn_readfirstlane(e0 + (r1 & dke1) + (r2 & dke2) + (r3 & dke3));
     return d;
   };
   // Where a tile's 64 rows live: the source (cache or segment), a uniform
@@ -292,12 +293,12 @@ __global__ void __launch_bounds__(256, 2) prefill_chunk_d128_kernel(CkArgs a, Ch
   struct TileAddr {
     int vo[4];
     int so;
-    bool cache;
+    int cache;  // 1: the cache, 0: the segment
   };
   auto tile_addr = [&](const TileDesc& d) {
     TileAddr t;
     const int lim = d.kend - 1 - d.key0;  // the run's last row within the tile
-    t.cache = d.run == 0 || d.run == 2;
+    t.cache = (d.run & 1) ^ 1;
     if (d.run < 2) {
       // summaries: slot sum0 + j in the cache, row j (k+1) + k - a0 in the
       // segment, both affine in j
@@ -327,7 +328,7 @@ __global__ void __launch_bounds__(256, 2) prefill_chunk_d128_kernel(CkArgs a, Ch
   };
   // a tile of K (is_v false) or V into buf, straight to LDS
   auto load_tile = [&](bool is_v, char* buf, const TileAddr& t) {
-    const __amdgpu_buffer_rsrc_t rs = t.cache ? (is_v ? rc_v : rc_k) : (is_v ? rs_v : rs_k);
+    const __amdgpu_buffer_rsrc_t rs = t.cache != 0 ? (is_v ? rc_v : rc_k) : (is_v ? rs_v : rs_k);
     const int so = t.so;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
