@@ -56,6 +56,7 @@ struct BwdArgs {
   float scale;  // softmax scale
   // dq kernel
   int32_t n_tiles, n_hg, n_sum_blocks;
+  int32_t n_kv_blocks;  // dkdv workgroups, ahead of the dq ones in the grid
   // dkdv kernel
   int32_t n_sum_wg;  // summary-key workgroups (all sequences and heads)
   int32_t nt_sum;    // 128-summary tiles per head
@@ -150,22 +151,22 @@ __device__ void summary_dq_wave(const BwdArgs& a, int64_t item, const bf16_t* __
 // dq of the text query rows.
 // ---------------------------------------------------------------------------
 template <int HPW>
-__global__ void __launch_bounds__(256, 2) bwd_dq_d128_kernel(
-    BwdArgs a, const bf16_t* __restrict__ q, const bf16_t* __restrict__ kx, const bf16_t* __restrict__ vx,
-    const bf16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
-    bf16_t* __restrict__ dq) {
+__device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int blk, const bf16_t* __restrict__ q,
+                                            const bf16_t* __restrict__ kx, const bf16_t* __restrict__ vx,
+                                            const bf16_t* __restrict__ dout, const float* __restrict__ lse,
+                                            const float* __restrict__ delta, bf16_t* __restrict__ dq, char* lds) {
   constexpr int PT = 32 * (4 / HPW);  // text positions per workgroup
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if (static_cast<int>(blockIdx.x) < a.n_sum_blocks) {
-    const int64_t item = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  if (blk < a.n_sum_blocks) {
+    const int64_t item = static_cast<int64_t>(blk) * 4 + wave;
     if (item < static_cast<int64_t>(a.batch) * a.hkv * a.M)
       summary_dq_wave(a, item, q, kx, vx, dout, lse, delta, dq);
     return;
   }
   const int n_slots = a.batch * a.hkv * a.n_hg;
-  const int bid = blockIdx.x - a.n_sum_blocks;
+  const int bid = blk - a.n_sum_blocks;
   const int hslot = bid % n_slots;
   const int tile = a.n_tiles - 1 - bid / n_slots;  // longest first
   const int hg = hslot % a.n_hg;
@@ -227,12 +228,8 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_d128_kernel(
   const int chunk16 = 16 * (ld_chunk ^ lds_swz(ld_row));
   const int sum_step = (a.k + 1) * RB;
   const int s_c0 = ld_row * sum_step + a.k * RB + chunk16;
-  __shared__ __attribute__((aligned(16))) char lds_k0[TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) char lds_k1[TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) char lds_v0[TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) char lds_v1[TILE_BYTES];
-  char* const lds_k[2] = {lds_k0, lds_k1};
-  char* const lds_v[2] = {lds_v0, lds_v1};
+  char* const lds_k[2] = {lds, lds + TILE_BYTES};
+  char* const lds_v[2] = {lds + 2 * TILE_BYTES, lds + 3 * TILE_BYTES};
   // rows past a run's end are masked or, past the sequence, read as zeros;
   // when k divides 64 a text tile starts 64 + 64/k rows after the previous
   int t_base[4];
@@ -372,16 +369,17 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_d128_kernel(
 // ---------------------------------------------------------------------------
 // dk, dv: keys fixed per workgroup, query tiles streamed.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256, 2) bwd_dkdv_d128_kernel(
-    BwdArgs a, const bf16_t* __restrict__ q, const bf16_t* __restrict__ kx, const bf16_t* __restrict__ vx,
-    const bf16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
-    bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, float* __restrict__ part) {
+__device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a, int blk, const bf16_t* __restrict__ q,
+                                              const bf16_t* __restrict__ kx, const bf16_t* __restrict__ vx,
+                                              const bf16_t* __restrict__ dout, const float* __restrict__ lse,
+                                              const float* __restrict__ delta, bf16_t* __restrict__ dk,
+                                              bf16_t* __restrict__ dv, float* __restrict__ part, char* lds) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int half = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nbh = a.batch * a.hkv;
-  const int bid = blockIdx.x;
+  const int bid = blk;
   const bool sum_keys = bid < a.n_sum_wg;
   int b, kvh, key0, u = 0, nkeys;
   // query runs: text positions [qt0, qt1) in 64-row tiles, then (text keys
@@ -449,21 +447,29 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_d128_kernel(
       vop[ks] = *reinterpret_cast<const bf16x8_t*>(vx + o + 16 * ks);
     }
   }
-  // Queries that see the lane's key, as index ranges of each query kind:
-  // text queries [tq_lo, tq_hi], summary queries [sq_lo, sq_hi].
+  // Queries that see the lane's key, as an index range [lo, hi] of the text
+  // queries or of the summary queries (sq):
   //   text key x, chunk c:  text x .. (c+C+1)k - 1 (or x + W - 1), summary c
   //   summary key j:        text (j+C+1)k .. n - 1
-  const int kc = div_k(a, key_valid ? key : key0);
-  int tq_lo, tq_hi, sq_lo = 0, sq_hi = -1;
-  if (sum_keys) {
-    tq_lo = (key + a.C + 1) * a.k;
-    tq_hi = key_valid ? qt1 - 1 : -1;
-  } else {
-    tq_lo = key;
-    tq_hi = !key_valid ? -1 : min(qt1 - 1, a.mode == KSA_MODE_SWA ? key + a.W - 1 : (kc + a.C + 1) * a.k - 1);
-    sq_lo = kc;
-    sq_hi = key_valid && kc <= cs1 ? kc : -1;
-  }
+  // Formed per masked tile from an opaque copy of the lane: kept across the
+  // loop, these per-lane bounds are spilled.
+  auto key_bounds = [&](bool sq, int* lo, int* hi) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int kl = kw0 + (ln & 31);
+    const bool kv = kl < key0 + nkeys;
+    const int kc = div_k(a, kv ? kl : key0);
+    if (sum_keys) {
+      *lo = (kl + a.C + 1) * a.k;
+      *hi = kv ? qt1 - 1 : -1;
+    } else if (sq) {
+      *lo = kc;
+      *hi = kv && kc <= cs1 ? kc : -1;
+    } else {
+      *lo = kl;
+      *hi = !kv ? -1 : min(qt1 - 1, a.mode == KSA_MODE_SWA ? kl + a.W - 1 : (kc + a.C + 1) * a.k - 1);
+    }
+  };
   // wave-uniform: the smallest key's upper bound, the largest key
   const int kwl = min(kw0 + 31, key0 + nkeys - 1);
   const int whi_min = sum_keys ? 0 : a.mode == KSA_MODE_SWA ? kw0 + a.W - 1 : (div_k(a, kw0) + a.C + 1) * a.k - 1;
@@ -471,13 +477,9 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_d128_kernel(
   // Q / dO tiles: 64 rows of one query head, rows gathered by the Eq. 1 map.
   const int qhs = a.hq * D;  // elements per augmented row
   const int QRB = qhs * 2;
-  __shared__ __attribute__((aligned(16))) char lds_q0[TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) char lds_q1[TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) char lds_g0[TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) char lds_g1[TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) float lds_st[2][2][BN];  // [buffer][lse, delta][row]
-  char* const lds_q[2] = {lds_q0, lds_q1};
-  char* const lds_g[2] = {lds_g0, lds_g1};
+  char* const lds_q[2] = {lds, lds + TILE_BYTES};
+  char* const lds_g[2] = {lds + 2 * TILE_BYTES, lds + 3 * TILE_BYTES};
+  float(*const lds_st)[2][BN] = reinterpret_cast<float(*)[2][BN]>(lds + 4 * TILE_BYTES);  // [buffer][lse, delta][row]
   const int64_t qbase = static_cast<int64_t>(b) * a.L * qhs;
   // iteration it -> (head, kind, first query index of the tile)
   auto tile_of = [&](int it, int* h, bool* sq, int* i0) {
@@ -564,7 +566,12 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_d128_kernel(
     (void)h;
     const char* ql = lds_q[cur];
     const char* gl = lds_g[cur];
-    const float* st = &lds_st[cur][0][0];
+    // this lane's rows of the statistics: the lane part comes from an opaque
+    // copy, so the reads take one address register and immediate offsets
+    // (left visible, their addresses are formed ahead and spilled)
+    int hb = 4 * half;
+    asm volatile("" : "+v"(hb));
+    const float* st = &lds_st[cur][0][0] + hb;
     // full: every row of the tile is a query of the run and sees every key
     // of the wave (the first row the largest key, the last row the smallest)
     bool full;
@@ -575,8 +582,12 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_d128_kernel(
     else
       full = i0 + BN - 1 < qt1 && i0 >= kwl && i0 + BN - 1 <= whi_min;
     const int base = i0 + 4 * half;
-    const int lo = (sq ? sq_lo : tq_lo) - base;
-    const int hi = (sq ? sq_hi : tq_hi) - base;
+    int lo = 0, hi = -1;
+    if (!full) {
+      key_bounds(sq, &lo, &hi);
+      lo -= base;
+      hi -= base;
+    }
     // two halves of 32 query rows, one after the other (keeps the live
     // registers within two waves per SIMD)
 #pragma unroll
@@ -603,7 +614,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_d128_kernel(
       float p[16];
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(st + 32 * blk + 8 * r4 + 4 * half);
+        const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(st + 32 * blk + 8 * r4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) p[4 * r4 + e] = fast_exp2(s[4 * r4 + e] * a.sl - l4[e] * kLog2e);
       }
@@ -619,8 +630,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_d128_kernel(
       u32x4_t pw[2], dw[2];
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const int row = 32 * blk + 8 * r4 + 4 * half;
-        const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(st + BN + row);
+        const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(st + BN + 32 * blk + 8 * r4);
         float ds[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) ds[e] = p[4 * r4 + e] * (dp[4 * r4 + e] - d4[e]);
@@ -696,6 +706,27 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_d128_kernel(
         *reinterpret_cast<uint2*>(dv + o + d) = wv;
       }
   }
+}
+
+// ---------------------------------------------------------------------------
+// One launch for both: the dkdv workgroups (the long summary-key ones first)
+// take the first block indices and the dq workgroups follow, so dq work fills
+// the machine while the last dkdv workgroups finish.  The two share one LDS
+// buffer (each uses four 16 KB tiles; dkdv adds its row statistics).
+// ---------------------------------------------------------------------------
+constexpr int BWD_LDS_BYTES = 4 * TILE_BYTES + 2 * 2 * BN * static_cast<int>(sizeof(float));
+
+template <int HPW>
+__global__ void __launch_bounds__(256, 2) bwd_dkdv_dq_kernel(
+    BwdArgs a, const bf16_t* __restrict__ q, const bf16_t* __restrict__ kx, const bf16_t* __restrict__ vx,
+    const bf16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
+    bf16_t* __restrict__ dq, bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) char lds[BWD_LDS_BYTES];
+  const int bid = blockIdx.x;
+  if (bid < a.n_kv_blocks)
+    bwd_dkdv_body(a, bid, q, kx, vx, dout, lse, delta, dk, dv, part, lds);
+  else
+    bwd_dq_body<HPW>(a, bid - a.n_kv_blocks, q, kx, vx, dout, lse, delta, dq, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -824,46 +855,33 @@ size_t prefill_bwd_mfma_partial_bytes(const PrefillArgs& p) {
 }
 
 template <int HPW>
-static hipError_t launch_dq(BwdArgs a, const void* q, const void* k, const void* v, const void* dout,
-                            const float* lse, const float* delta, void* dq, hipStream_t s) {
+static hipError_t launch_main(BwdArgs a, const void* q, const void* k, const void* v, const void* dout,
+                              const float* lse, const float* delta, float* part, void* dq, void* dk, void* dv,
+                              hipStream_t s) {
   constexpr int PT = 32 * (4 / HPW);
+  // dq: summary query waves, then text tiles
   a.n_hg = a.g / HPW;
   a.n_tiles = (a.n + PT - 1) / PT;
   const int64_t n_slots = static_cast<int64_t>(a.batch) * a.hkv * a.n_hg;
   const int64_t sum_items = static_cast<int64_t>(a.batch) * a.hkv * a.M;
   a.n_sum_blocks = static_cast<int32_t>((sum_items + 3) / 4);
-  const int64_t blocks = n_slots * a.n_tiles + a.n_sum_blocks;
-  if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(bwd_dq_d128_kernel<HPW>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, s, a,
-                     static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v),
-                     static_cast<const bf16_t*>(dout), lse, delta, static_cast<bf16_t*>(dq));
-  return hipGetLastError();
-}
-
-hipError_t launch_prefill_bwd_mfma(const PrefillArgs& p, const void* q, const void* k, const void* v,
-                                   const void* dout, const float* lse, const float* delta, float* part,
-                                   void* dq, void* dk, void* dv, hipStream_t s) {
-  BwdArgs a = make_args(p);
-  hipError_t e;
-  if (a.g == 1)
-    e = launch_dq<1>(a, q, k, v, dout, lse, delta, dq, s);
-  else if (a.g == 2)
-    e = launch_dq<2>(a, q, k, v, dout, lse, delta, dq, s);
-  else
-    e = launch_dq<4>(a, q, k, v, dout, lse, delta, dq, s);
-  if (e != hipSuccess) return e;
-
+  const int64_t dq_blocks = n_slots * a.n_tiles + a.n_sum_blocks;
+  // dkdv: summary-key workgroups per query segment, then text keys
   const int64_t nbh = static_cast<int64_t>(a.batch) * a.hkv;
   int64_t per_head = 0;
   if (a.mode == KSA_MODE_KSA)
     for (int u = 0; u < a.nu; ++u) per_head += seg_tiles_host(a, u);
   a.n_sum_wg = static_cast<int32_t>(per_head * nbh);
   const int64_t text_wg = nbh * ((a.n + KW - 1) / KW);
-  hipLaunchKernelGGL(bwd_dkdv_d128_kernel, dim3(static_cast<uint32_t>(a.n_sum_wg + text_wg)), dim3(256), 0, s, a,
+  a.n_kv_blocks = static_cast<int32_t>(a.n_sum_wg + text_wg);
+  const int64_t blocks = a.n_kv_blocks + dq_blocks;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(bwd_dkdv_dq_kernel<HPW>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, s, a,
                      static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v),
-                     static_cast<const bf16_t*>(dout), lse, delta, static_cast<bf16_t*>(dk),
-                     static_cast<bf16_t*>(dv), part);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+                     static_cast<const bf16_t*>(dout), lse, delta, static_cast<bf16_t*>(dq),
+                     static_cast<bf16_t*>(dk), static_cast<bf16_t*>(dv), part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const int64_t items = nbh * a.M;
   if (items == 0) return hipSuccess;
   hipLaunchKernelGGL(bwd_sum_keys_kernel, dim3(static_cast<uint32_t>((items + 3) / 4)), dim3(256), 0, s, a,
@@ -871,6 +889,15 @@ hipError_t launch_prefill_bwd_mfma(const PrefillArgs& p, const void* q, const vo
                      static_cast<const bf16_t*>(dout), lse, delta, part, static_cast<bf16_t*>(dk),
                      static_cast<bf16_t*>(dv));
   return hipGetLastError();
+}
+
+hipError_t launch_prefill_bwd_mfma(const PrefillArgs& p, const void* q, const void* k, const void* v,
+                                   const void* dout, const float* lse, const float* delta, float* part,
+                                   void* dq, void* dk, void* dv, hipStream_t s) {
+  const BwdArgs a = make_args(p);
+  if (a.g == 1) return launch_main<1>(a, q, k, v, dout, lse, delta, part, dq, dk, dv, s);
+  if (a.g == 2) return launch_main<2>(a, q, k, v, dout, lse, delta, part, dq, dk, dv, s);
+  return launch_main<4>(a, q, k, v, dout, lse, delta, part, dq, dk, dv, s);
 }
 
 }  // namespace ksa
