@@ -12,7 +12,8 @@
 // integer compares on chunk indices.  A summary query s_j reads only its own
 // chunk's k text tokens and itself (Sec. 2.2.1), i.e. the k+1 consecutive
 // augmented rows j(k+1) .. j(k+1)+k; those rows are handled by the first
-// workgroups of the same launch (one wave per summary and kv head).
+// workgroups of the same launch (a wave per four summaries and kv head
+// when k <= 8, else per summary).
 //
 // Text workgroups (4 wavefronts, 256 threads):
 //   - a workgroup owns one kv head and HPW of its query heads over PT
@@ -53,6 +54,9 @@ using namespace mfma;
 constexpr int BN = 64;            // keys per tile
 constexpr int TILE_BYTES = BN * ROW_BYTES;
 constexpr float kLazyRescale = 8.f;  // log2 units
+// Byte range of the query-row buffer resource: above every in-range offset
+// (fewer than 64 augmented rows of Hq heads after the wave's first row).
+constexpr int kQRange = 1 << 30;
 
 struct MfmaArgs {
   int32_t batch, n, L, k, C, hq, hkv, g, M;
@@ -99,11 +103,9 @@ __device__ __forceinline__ int32_t trow(const MfmaArgs& a, int32_t t) { return t
 // the group's query heads to the k + 1 rows j(k+1) .. j(k+1)+k.  Lane
 // (hh, c) = (lane / 16, lane % 16) holds dims 8c .. 8c+7 of head hh of a
 // group of four; the key/value rows of a pass are all loaded before any is
-// used, so a pass costs one memory round trip.  SUM_R key rows per pass: 9
-// (one pass) when k <= 8, else 16; rows past the chunk are masked but their
-// loads and dot products are still paid, so the pass is sized to the chunk
-// (at k = 8 a 16-row pass spent 7/16 of this path's vector work on masked
-// rows, and the summary rows took 80 of 1441 us of the 32K prefill).
+// used, so a pass costs one memory round trip.  SUM_R = 16 key rows per
+// pass; rows past the chunk are masked.  This path serves k > 8; for
+// k <= 8, summary_rows_wave_multi below.
 template <int SUM_R, bool QROT>
 __device__ void summary_rows_wave(const MfmaArgs& a, int64_t item, const bf16_t* __restrict__ q,
                                   const bf16_t* __restrict__ kx, const bf16_t* __restrict__ vx,
@@ -202,6 +204,154 @@ __device__ void summary_rows_wave(const MfmaArgs& a, int64_t item, const bf16_t*
   }
 }
 
+// Summary query rows for k <= 8, several per wave: a wave attends
+// kSumPerWave consecutive (summary, head group) units, the next unit's key,
+// value and query rows loaded while the current one is computed, so a wave
+// pays one memory round trip for all of them.  The summary workgroups run
+// two per CU (the launch's LDS allocation), first in the launch; with one
+// summary per wave the 8192 of them filled about the first 65 us of the
+// 32K prefill, with four about 50 us (per-workgroup timestamps).  Unit u
+// is summary j of (sequence, kv head) item u / n_hgrp and head group
+// 4 (u % n_hgrp); lane (hh, c) holds dims 8c .. 8c+7 of head hh of the
+// group; the k + 1 rows j(k+1) .. j(k+1)+k are read as 9 rows, rows past
+// the chunk repeating its last row and masked.  The arithmetic is that of
+// summary_rows_wave's single pass.
+constexpr int kSumPerWave = 4;
+
+struct SumUnitRows {
+  u32x4_t qw, kw[9], vw[9];
+};
+
+template <bool QROT>
+__device__ void summary_rows_wave_multi(const MfmaArgs& a, int64_t u0, int64_t n_units,
+                                        const bf16_t* __restrict__ q, const bf16_t* __restrict__ kx,
+                                        const bf16_t* __restrict__ vx, bf16_t* __restrict__ out,
+                                        float* __restrict__ lse) {
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 15;
+  const int hh = lane >> 4;
+  const int n_hgrp = (a.g + 3) >> 2;
+  const int64_t kvs = static_cast<int64_t>(a.hkv) * D;
+  // this lane's rotation rate (frequency lane), read before any row load:
+  // a wait for a later-issued load would also wait for every row load
+  // issued before it
+  uint64_t fq_lane = 0;
+  if constexpr (QROT) fq_lane = a.rope_fq[lane];
+  __builtin_amdgcn_sched_barrier(0);
+  struct Unit {
+    int b, kvh, j, hg;
+  };
+  // Units past the last are read and computed as the last one (the same
+  // values stored again): the loop below has no branch, so every wait for a
+  // unit's rows counts exactly the row loads issued after them.
+  const uint32_t u_last = static_cast<uint32_t>(n_units - 1);
+  auto unit_of = [&](int64_t u) {
+    const uint32_t uc = static_cast<uint32_t>(u) < u_last ? static_cast<uint32_t>(u) : u_last;
+    Unit t;
+    const uint32_t item = uc / static_cast<uint32_t>(n_hgrp);
+    t.hg = 4 * static_cast<int>(uc - item * n_hgrp);
+    const uint32_t bk = item / static_cast<uint32_t>(a.M);
+    t.j = static_cast<int>(item - bk * a.M);
+    t.b = static_cast<int>(bk / static_cast<uint32_t>(a.hkv));
+    t.kvh = static_cast<int>(bk - t.b * a.hkv);
+    return t;
+  };
+  auto head_of = [&](const Unit& t) {
+    const int hloc = t.hg + hh;
+    return t.kvh * a.g + (hloc < a.g ? hloc : 0);
+  };
+  auto load = [&](const Unit& t, SumUnitRows& r) __attribute__((always_inline)) {
+    const int r0 = t.j * (a.k + 1);
+    const int srow_a = r0 + a.k;
+    r.qw = *reinterpret_cast<const u32x4_t*>(q + (static_cast<int64_t>(t.b) * a.L + srow_a) * a.hq * D +
+                                             static_cast<int64_t>(head_of(t)) * D + 8 * c);
+    const bf16_t* kb = kx + static_cast<int64_t>(t.b) * a.L * kvs + t.kvh * D + 8 * c;
+    const bf16_t* vb = vx + static_cast<int64_t>(t.b) * a.L * kvs + t.kvh * D + 8 * c;
+#pragma unroll
+    for (int i = 0; i < 9; ++i) {
+      const int row = r0 + min(i, a.k);
+      r.kw[i] = *reinterpret_cast<const u32x4_t*>(kb + row * kvs);
+      r.vw[i] = *reinterpret_cast<const u32x4_t*>(vb + row * kvs);
+    }
+  };
+  auto compute = [&](const Unit& t, SumUnitRows& r) __attribute__((always_inline)) {
+    const int srow_a = t.j * (a.k + 1) + a.k;
+    const int h = head_of(t);
+    u32x4_t qw = r.qw;
+    if constexpr (QROT) {
+      // position of s_j: its chunk's last text token; dims 8c .. 8c+7 pair
+      // with dims 8c +- 64, which lane c ^ 8 of the same 16 holds; lane l
+      // forms angle l and each lane gathers its eight with ds_bpermute
+      float sn_l, cs_l;
+      rope_sincos(static_cast<uint32_t>((t.j + 1) * a.k - 1), fq_lane, &sn_l, &cs_l);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t y = static_cast<uint32_t>(
+            __builtin_amdgcn_update_dpp(0, static_cast<int>(qw[w]), 0x128, 0xF, 0xF, false));  // row_ror:8
+        const int f0 = 4 * (8 * (c & 7) + 2 * w);  // byte address of lane f
+        const float sn0 = __int_as_float(__builtin_amdgcn_ds_bpermute(f0, __float_as_int(sn_l)));
+        const float cs0 = __int_as_float(__builtin_amdgcn_ds_bpermute(f0, __float_as_int(cs_l)));
+        const float sn1 = __int_as_float(__builtin_amdgcn_ds_bpermute(f0 + 4, __float_as_int(sn_l)));
+        const float cs1 = __int_as_float(__builtin_amdgcn_ds_bpermute(f0 + 4, __float_as_int(cs_l)));
+        qw[w] = rope_pair(qw[w], y, c >= 8, sn0, cs0, sn1, cs1);
+      }
+    }
+    float sc[9];
+    float mx = kNegInf;
+#pragma unroll
+    for (int i = 0; i < 9; ++i) {
+      float part = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qw.x), as_bf16x2(r.kw[i].x), 0.f, false);
+      part = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qw.y), as_bf16x2(r.kw[i].y), part, false);
+      part = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qw.z), as_bf16x2(r.kw[i].z), part, false);
+      part = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qw.w), as_bf16x2(r.kw[i].w), part, false);
+      part = sum16(part);
+      sc[i] = i <= a.k ? part * a.sl : kNegInf;
+      mx = fmaxf(mx, sc[i]);
+    }
+    float l = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 9; ++i) {
+      const float p = fast_exp2(sc[i] - mx);
+      l += p;
+      const u32x4_t w = r.vw[i];
+      o[0] += p * bf_lo(w.x); o[1] += p * bf_hi(w.x);
+      o[2] += p * bf_lo(w.y); o[3] += p * bf_hi(w.y);
+      o[4] += p * bf_lo(w.z); o[5] += p * bf_hi(w.z);
+      o[6] += p * bf_lo(w.w); o[7] += p * bf_hi(w.w);
+    }
+    if (t.hg + hh < a.g) {
+      const float inv = 1.f / l;
+      u32x4_t ow;
+      ow.x = pk_bf16(o[0] * inv, o[1] * inv);
+      ow.y = pk_bf16(o[2] * inv, o[3] * inv);
+      ow.z = pk_bf16(o[4] * inv, o[5] * inv);
+      ow.w = pk_bf16(o[6] * inv, o[7] * inv);
+      *reinterpret_cast<u32x4_t*>(out + (static_cast<int64_t>(t.b) * a.L + srow_a) * a.hq * D +
+                                  static_cast<int64_t>(h) * D + 8 * c) = ow;
+      if (lse && c == 0)
+        lse[(static_cast<int64_t>(t.b) * a.hq + h) * a.L + srow_a] = (mx + log2f(l)) * kLn2;
+    }
+  };
+  // two register sets in turn, in straight-line code: unit i + 1 loads
+  // while unit i is computed; the scheduling barriers keep the compiler
+  // from hoisting later units' loads (which would need a third set)
+  if (u0 >= n_units) return;
+  Unit ut[2];
+  SumUnitRows rs[2];
+  ut[0] = unit_of(u0);
+  load(ut[0], rs[0]);
+#pragma unroll
+  for (int i = 0; i < kSumPerWave; ++i) {
+    if (i + 1 < kSumPerWave) {
+      ut[(i + 1) & 1] = unit_of(u0 + i + 1);
+      load(ut[(i + 1) & 1], rs[(i + 1) & 1]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    compute(ut[i & 1], rs[i & 1]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 }  // namespace
 
 template <int HPW, bool QROT>
@@ -210,16 +360,23 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_d128_kernel(
     const bf16_t* __restrict__ vx, bf16_t* __restrict__ out, float* __restrict__ lse) {
   constexpr int PT = 32 * (4 / HPW);  // text positions per workgroup
 
+  // Every argument the set-up reads, named at once: the compiler reads a
+  // kernel argument where it is first used, and through the branches of the
+  // set-up below that was a chain of scalar-load round trips; an empty asm
+  // that takes them all in scalar registers makes it one round of loads.
+  asm volatile("" ::"s"(a.batch), "s"(a.n), "s"(a.L), "s"(a.k), "s"(a.C), "s"(a.hq), "s"(a.hkv), "s"(a.g),
+               "s"(a.M), "s"(a.n_tiles), "s"(a.n_hg), "s"(a.xcd_map), "s"(a.n_sum_blocks), "s"(a.divk_m),
+               "s"(a.divk_l), "s"(a.sl), "s"(a.mode), "s"(a.W));
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   if (static_cast<int>(blockIdx.x) < a.n_sum_blocks) {
-    const int64_t item = static_cast<int64_t>(blockIdx.x) * 4 + wave;
-    if (item < static_cast<int64_t>(a.batch) * a.hkv * a.M) {
-      if (a.k <= 8)
-        summary_rows_wave<9, QROT>(a, item, q, kx, vx, out, lse);
-      else
-        summary_rows_wave<16, QROT>(a, item, q, kx, vx, out, lse);
+    const int64_t wid = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+    const int64_t n_items = static_cast<int64_t>(a.batch) * a.hkv * a.M;
+    if (a.k <= 8) {
+      summary_rows_wave_multi<QROT>(a, wid * kSumPerWave, n_items * ((a.g + 3) >> 2), q, kx, vx, out, lse);
+    } else if (wid < n_items) {
+      summary_rows_wave<16, QROT>(a, wid, q, kx, vx, out, lse);
     }
     return;
   }
@@ -270,16 +427,21 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_d128_kernel(
   const int tlo_w1 = text_lo(wave_active ? iw1 : 0, cw1);
 
   // Q^T as the B operand: column = query (lane % 32), k-slots
-  // d = 16 ks + 8 (lane / 32) + j.
+  // d = 16 ks + 8 (lane / 32) + j.  The rows are read through a buffer
+  // resource based at the wave's first query row: a lane past the sequence
+  // end gets an offset beyond the resource's range and reads zeros, so no
+  // branch (and no wait for these loads) comes before the tile loads below.
   const int half = lane >> 5;
   bf16x8_t qop[8];
   {
-    const int qrow = trow(a, q_valid ? qi : 0);
-    const bf16_t* qp =
-        q + (static_cast<int64_t>(b) * a.L + qrow) * a.hq * D + static_cast<int64_t>(h) * D + 8 * half;
+    const int qrow0 = trow(a, wave_active ? iw0 : 0);
+    const __amdgpu_buffer_rsrc_t rsrc_q = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<bf16_t*>(q + (static_cast<int64_t>(b) * a.L + qrow0) * a.hq * D + static_cast<int64_t>(h) * D),
+        static_cast<short>(0), kQRange, 0x00020000);
+    const int qoff = q_valid ? (trow(a, qi) - qrow0) * a.hq * ROW_BYTES + 16 * half : kQRange;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
-      qop[ks] = q_valid ? *reinterpret_cast<const bf16x8_t*>(qp + 16 * ks) : bf16x8_t{};
+      qop[ks] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc_q, qoff + 32 * ks, 0, 0));
   }
 
   // Tile loads: thread owns 16-byte chunk (tid % 16) of rows tid/16 + 16 u
@@ -493,34 +655,38 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_d128_kernel(
   };
 
   f32x16_t sa[2], sb[2];
+  // Query rotation: text t_qi sits at position qi; dims f = 16 ks + 8 half
+  // + j (ks < 4) and f + 64 are both in this lane.  (sin, cos) of the
+  // angle of (position, f): with four heads per block all waves hold the
+  // same 32 positions, so each thread forms 8 of the 32 x 64 pairs into
+  // the second V buffer (not yet in use: the barrier before the loop orders
+  // these reads before its first load) and every lane reads its 32;
+  // otherwise each lane forms its own.  The table is written before the
+  // first tile loads are issued (LDS accesses after a direct-to-LDS load
+  // wait for it), so it is ready when the query rows arrive.
+  [[maybe_unused]] float2* const tab = reinterpret_cast<float2*>(lds_v1);  // [f][position in the block's 32]
+  if constexpr (QROT && HPW == 4) {
+    static_assert(64 * 32 * sizeof(float2) <= TILE_BYTES, "the table fits one tile buffer");
+    // thread (tp, fg) forms frequencies 8 fg .. 8 fg + 7, fg = 2 wave +
+    // half, from wave-uniform (scalar) reads of the rates
+    const int tp = tid & 31, fg = tid >> 5;
+    const uint32_t pos = static_cast<uint32_t>(iw0 + tp);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint64_t f_lo = a.rope_fq[16 * wave + j], f_hi = a.rope_fq[16 * wave + 8 + j];
+      float sn, cs;
+      rope_sincos(pos, half ? f_hi : f_lo, &sn, &cs);
+      tab[(8 * fg + j) * 32 + tp] = make_float2(sn, cs);
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this thread's table writes are done
+    __builtin_amdgcn_s_barrier();
+  }
   if (n_total > 0) {
     load_tile(rsrc_k, lds_k[0], 0);
     load_tile(rsrc_v, lds_v[0], 0);
     load_tile(rsrc_k, lds_k[1], n_total > 1 ? 1 : 0);
   }
   if constexpr (QROT) {
-    // Query rotation: text t_qi sits at position qi; dims f = 16 ks + 8 half
-    // + j (ks < 4) and f + 64 are both in this lane.  (sin, cos) of the
-    // angle of (position, f): with four heads per block all waves hold the
-    // same 32 positions, so each thread forms 8 of the 32 x 64 pairs into
-    // the second V buffer (not yet in use: the barrier before the loop
-    // orders these reads before its first load) and every lane reads its
-    // 32; otherwise each lane forms its own.  This runs while the first
-    // tiles are in flight: its barrier waits for LDS writes only.
-    float2* const tab = reinterpret_cast<float2*>(lds_v1);  // [f][position in the block's 32]
-    if constexpr (HPW == 4) {
-      static_assert(64 * 32 * sizeof(float2) <= TILE_BYTES, "the table fits one tile buffer");
-      const int tp = tid & 31, fg = tid >> 5;
-      const uint32_t pos = static_cast<uint32_t>(iw0 + tp);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float sn, cs;
-        rope_sincos(pos, a.rope_fq[8 * fg + j], &sn, &cs);
-        tab[(8 * fg + j) * 32 + tp] = make_float2(sn, cs);
-      }
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this thread's table writes are done
-      __builtin_amdgcn_s_barrier();
-    }
     const uint32_t pos = static_cast<uint32_t>(qi);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -533,8 +699,9 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_d128_kernel(
           const float2 e0 = tab[f * 32 + (lane & 31)], e1 = tab[(f + 1) * 32 + (lane & 31)];
           sn0 = e0.x, cs0 = e0.y, sn1 = e1.x, cs1 = e1.y;
         } else {
-          rope_sincos(pos, a.rope_fq[f], &sn0, &cs0);
-          rope_sincos(pos, a.rope_fq[f + 1], &sn1, &cs1);
+          const int fu = 16 * ks + 2 * w;  // f without the lane half, wave-uniform
+          rope_sincos(pos, half ? a.rope_fq[fu + 8] : a.rope_fq[fu], &sn0, &cs0);
+          rope_sincos(pos, half ? a.rope_fq[fu + 9] : a.rope_fq[fu + 1], &sn1, &cs1);
         }
         const uint32_t x = lo[w], y = hi[w];
         lo[w] = rope_pair(x, y, false, sn0, cs0, sn1, cs1);
@@ -645,7 +812,11 @@ static hipError_t launch_hpw(const PrefillArgs& p, const void* q, const void* k,
   a.mode = p.mode;
   a.W = static_cast<int32_t>(p.window_tokens);
   const int64_t sum_items = static_cast<int64_t>(a.batch) * a.hkv * a.M;
-  a.n_sum_blocks = static_cast<int32_t>(((sum_items + 3) / 4 + 7) / 8 * 8);  // keeps text blocks XCD-aligned
+  // waves of summary rows: kSumPerWave (summary, head group) units each
+  // when k <= 8, else one summary with all head groups
+  const int64_t sum_waves =
+      p.k <= 8 ? (sum_items * ((a.g + 3) / 4) + kSumPerWave - 1) / kSumPerWave : sum_items;
+  a.n_sum_blocks = static_cast<int32_t>(((sum_waves + 3) / 4 + 7) / 8 * 8);  // keeps text blocks XCD-aligned
   const bool qrot = p.rope_theta > 0.0;
   for (int f = 0; f < 64; ++f) {
     // theta^(-2f/128) / (2 pi) revolutions per position, below 1/6, as a
