@@ -124,6 +124,7 @@ BF16_CASES = [
     (257, 1, 2, 8, 1),
     (33, 8, 1, 4, 1),
     (7, 8, 2, 4, 1),
+    (75, 8, 2, 2, 1),   # 18 summary units: the last summary wave repeats its last unit
 ]
 
 
