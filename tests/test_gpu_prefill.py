@@ -125,6 +125,7 @@ BF16_CASES = [
     (33, 8, 1, 4, 1),
     (7, 8, 2, 4, 1),
     (75, 8, 2, 2, 1),   # 18 summary units: the last summary wave repeats its last unit
+    (600, 16, 3, 8, 2),  # k > 8: one summary per wave, its 17 rows in two passes
 ]
 
 

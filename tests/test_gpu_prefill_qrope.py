@@ -71,6 +71,7 @@ CASES = [
     (2100, 8, 16, 16, 4, 1e6),
     (301, 3, 0, 2, 1, 5e5),
     (33, 8, 1, 4, 1, 1e4),
+    (600, 16, 3, 8, 2, 1e6),   # k > 8: the summary rows' rotation on the one-summary-per-wave path
 ]
 
 
