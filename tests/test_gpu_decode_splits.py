@@ -147,10 +147,14 @@ def _mla_codes(rows):
     return [rows % 256, 256 + (rows // 128) % 256]
 
 
-@pytest.mark.parametrize("ns_text,C", [([45003, 38005, 52007], 4), ([3003, 2505], 2), ([700, 1900, 130, 2600], 64)])
-def test_mla_decode_rows_exact_multi_range(ns_text, C):
+@pytest.mark.parametrize("ns_text,C,min_ranges", [
+    ([45003, 38005, 52007], 4, 4), ([3003, 2505], 2, 4), ([700, 1900, 130, 2600], 64, 4),
+    # more sequences than a wave has lanes: the cut is formed 64 sequences at a time
+    ([int(x) for x in np.random.default_rng(11).integers(40, 6000, 100)], 8, 2),
+])
+def test_mla_decode_rows_exact_multi_range(ns_text, C, min_ranges):
     """Ranges cut across a ragged batch: long slices (rows per range above
-    64), short ones (64-row ranges) and a wide window."""
+    64), short ones (64-row ranges), a wide window and a batch of 100."""
     dev = _dev()
     k = 8
     B = len(ns_text)
@@ -201,5 +205,5 @@ def test_mla_decode_rows_exact_multi_range(ns_text, C):
                 np.testing.assert_array_equal(cnt, want, err_msg=f"step {step} seq {b} head {h}")
             # every head reads the same rows
             np.testing.assert_array_equal(o[b], np.broadcast_to(o[b, 0], o[b].shape))
-    assert most_ranges >= 4
+    assert most_ranges >= min_ranges
     assert ksa.ksa_cache_read_errors(cache) == [0] * B
