@@ -148,6 +148,8 @@ def _chunk_case(dtype, D, n, k, C, hq, hkv, splits, seed):
     (torch.bfloat16, 128, 700, 8, 4, 8, 2),   # MFMA path
     (torch.bfloat16, 128, 530, 5, 3, 4, 4),   # MFMA path, g = 1, k = 5
     (torch.bfloat16, 128, 400, 8, 0, 4, 2),   # MFMA path, no ring
+    (torch.bfloat16, 128, 600, 8, 3, 16, 2),  # MFMA path, g = 8: two head groups per summary
+    (torch.bfloat16, 128, 500, 12, 2, 8, 2),  # MFMA path, k = 12: summary rows in two passes
     (torch.float32, 64, 300, 8, 2, 4, 2),     # generic path
 ])
 def test_chunked_prefill_matches_one_shot(dtype, D, n, k, C, hq, hkv):
@@ -191,6 +193,8 @@ def test_chunk_skips_sequences_with_bad_state(dtype, D):
         torch.cuda.synchronize()
         assert torch.isnan(out[L:].float()).all(), bad
         assert not torch.isnan(out[:L].float()).any(), bad
+        st = cache.state.cpu()
+        assert st[1, 3].item() & 16 and st[0, 3].item() == 0, (bad, st)  # KSA_CACHE_ERR_BAD_SEGMENT
 
 
 def test_chunked_prefill_absorbed_latent_generic():
