@@ -421,41 +421,44 @@ __global__ void __launch_bounds__(512, 1) decode_mla_split_kernel(
     }
 }
 
-// One block per (head, sequence): combine the ranges of the sequence by
-// their maxima; the head-0 block also flags a slice that cannot be read.
-// Every thread owns two output columns and reads, sixteen ranges at a time,
-// each range's (maximum, sum) and its two columns in one round of loads.
+// One wave per (head, sequence), four heads per block: combine the ranges of
+// the sequence by their maxima; the head-0 wave also flags a slice that
+// cannot be read.  Every lane owns eight output columns and reads, sixteen
+// ranges at a time, each range's (maximum, sum) and its eight columns in one
+// round of loads; the 1024 blocks of the 32 x 128 case fit the chip at once.
 __global__ void __launch_bounds__(256) decode_mla_merge_kernel(MlaArgs a, int32_t* __restrict__ state,
                                                                const int32_t* __restrict__ kind,
                                                                const char* __restrict__ ws,
                                                                bf16_t* __restrict__ out,
                                                                float* __restrict__ lse) {
-  const int head = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int head = 4 * blockIdx.x + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int b = blockIdx.y;
   // both loads in one round trip: the cut is written for every sequence
   const int kb = kind[b];
   const int2 cut = reinterpret_cast<const int2*>(ws + mla_cut_offset(a.max_items))[b];
   if (kb < 0) return;
-  if (head == 0 && threadIdx.x == 0 && !mla_slice(a, state + 4 * b, kb).ok)
+  if (head == 0 && lane == 0 && !mla_slice(a, state + 4 * b, kb).ok)
     state[4 * b + 3] |= KSA_CACHE_ERR_BAD_SUMMARY_READ;
   const int nsp = cut.y;
   const char* rec0 = ws + (static_cast<int64_t>(cut.x) * HQ + head) * kMlaRec;
   const int64_t stride = static_cast<int64_t>(HQ) * kMlaRec;
-  const int d = 2 * threadIdx.x;  // 256 threads x 2 columns = 512
-  float mx = kNegInf, l = 0.f, o0 = 0.f, o1 = 0.f;
+  const int d = 8 * lane;  // 64 lanes x 8 columns = 512
+  float mx = kNegInf, l = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   constexpr int G = 16;
   for (int s0 = 0; s0 < nsp; s0 += G) {
     float2 ml[G];
-    uint32_t v[G];
+    u32x2_t v[G][2];  // records are 8-byte aligned
 #pragma unroll
     for (int u = 0; u < G; ++u) {
       if (s0 + u < nsp) {
         const char* r = rec0 + (s0 + u) * stride;
         ml[u] = *reinterpret_cast<const float2*>(r);
-        v[u] = *reinterpret_cast<const uint32_t*>(r + 8 + 2 * d);
+        v[u][0] = *reinterpret_cast<const u32x2_t*>(r + 8 + 2 * d);
+        v[u][1] = *reinterpret_cast<const u32x2_t*>(r + 16 + 2 * d);
       } else {
         ml[u] = make_float2(kNegInf, 0.f);
-        v[u] = 0u;
+        v[u][0] = v[u][1] = (u32x2_t){0u, 0u};
       }
     }
     float gm = mx;
@@ -464,20 +467,27 @@ __global__ void __launch_bounds__(256) decode_mla_merge_kernel(MlaArgs a, int32_
     const float mu = gm == kNegInf ? 0.f : gm;
     const float sc = mx == kNegInf ? 0.f : fast_exp2(mx - mu);
     l *= sc;
-    o0 *= sc;
-    o1 *= sc;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] *= sc;
 #pragma unroll
     for (int u = 0; u < G; ++u) {
       const float w = ml[u].x == kNegInf ? 0.f : fast_exp2(ml[u].x - mu);
       l += w * ml[u].y;
-      o0 += w * __uint_as_float(v[u] << 16);
-      o1 += w * __uint_as_float(v[u] & 0xffff0000u);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t x = v[u][e >> 1][e & 1];
+        o[2 * e] += w * __uint_as_float(x << 16);
+        o[2 * e + 1] += w * __uint_as_float(x & 0xffff0000u);
+      }
     }
     mx = gm;
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  *reinterpret_cast<uint32_t*>(out + (static_cast<int64_t>(b) * HQ + head) * DV + d) = pk_bf16(o0 * inv, o1 * inv);
-  if (lse && threadIdx.x == 0)
+  u32x4_t ow;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) ow[e] = pk_bf16(o[2 * e] * inv, o[2 * e + 1] * inv);
+  *reinterpret_cast<u32x4_t*>(out + (static_cast<int64_t>(b) * HQ + head) * DV + d) = ow;
+  if (lse && lane == 0)
     lse[static_cast<int64_t>(b) * HQ + head] = l > 0.f ? (mx + log2f(l)) * kLn2 : kNegInf;
 }
 
@@ -513,7 +523,7 @@ hipError_t launch_decode_mla(const DecodeArgs& d, const void* ck, int32_t* state
                        static_cast<char*>(ws));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_mla_merge_kernel, dim3(HQ, d.batch), dim3(256), 0, s, a, state, kind,
+    hipLaunchKernelGGL(decode_mla_merge_kernel, dim3(HQ / 4, d.batch), dim3(256), 0, s, a, state, kind,
                        static_cast<const char*>(ws), static_cast<bf16_t*>(out), lse);
   }
   return hipGetLastError();
